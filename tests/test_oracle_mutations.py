@@ -1,0 +1,124 @@
+"""The pins catch plausible mistakes: plant each mistake in a copy of the
+oracle (on the CPU) and check that at least one pin rejects it, while the
+real oracle passes the same pins.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle.decode import GROUP_SIZE, decode_table, scale_decode_table
+from oracle.reduce import fp32_to_bf16_bits, reduce_scatter_share
+
+from test_oracle_closed_forms import build_example, load_worked_examples
+
+
+def _fold(xs, ss, xf, sl, out, *, order=None, start_zero=False, wide=False, pairwise=False, group=None,
+          to_bf16=fp32_to_bf16_bits):
+    """A configurable re-statement of the definition used only to plant mistakes."""
+    g = group or GROUP_SIZE[sl]
+    xt = decode_table(xf)
+    st = scale_decode_table()
+    ps = []
+    for x, s in zip(xs, ss):
+        sv = s if sl == "f32_group128" else st[s]
+        sv = np.repeat(sv, g, axis=1)[:, : x.shape[1]]
+        if sv.shape[1] < x.shape[1]:
+            sv = np.tile(sv, (1, x.shape[1] // sv.shape[1] + 1))[:, : x.shape[1]]
+        with np.errstate(over="ignore", invalid="ignore"):
+            if wide:
+                ps.append(xt[x].astype(np.float64) * sv.astype(np.float64))
+            else:
+                ps.append((xt[x] * sv).astype(np.float32))
+    if order is not None:
+        ps = [ps[i] for i in order(len(ps))]
+    if pairwise:
+        while len(ps) > 1:
+            ps = [ps[i] + ps[i + 1] if i + 1 < len(ps) else ps[i] for i in range(0, len(ps), 2)]
+        acc = ps[0]
+    else:
+        acc = np.zeros_like(ps[0]) if start_zero else ps[0]
+        for p in (ps if start_zero else ps[1:]):
+            acc = acc + p
+    acc = acc.astype(np.float32)
+    return acc if out == "f32" else to_bf16(acc)
+
+
+def _truncate_bf16(acc):
+    return (np.ascontiguousarray(acc).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _worked_examples_pass(fn):
+    for ex in load_worked_examples():
+        xs, ss = build_example(ex)
+        out = fn(xs, ss, ex["x_format"], ex["scale_layout"], ex["out_dtype"])
+        got = out.view(np.uint32) if ex["out_dtype"] == "f32" else out
+        if not np.all(got == int(ex["expected_bits"], 16)):
+            return False
+    return True
+
+
+def _cross_layout_passes(fn):
+    rng = np.random.default_rng(3)
+    wl = workloads.CONFIGS["C4"].with_(bs=8 * 2, h=1024)
+    xs, _ = workloads.generate(wl)
+    codes128 = [rng.integers(110, 145, size=(wl.rows, wl.h // 128), dtype=np.uint8) for _ in range(8)]
+    mx = [np.repeat(c, 4, axis=1) for c in codes128]
+    f32 = [np.ldexp(np.float32(1.0), c.astype(np.int32) - 127).astype(np.float32) for c in codes128]
+    a = fn(xs, mx, "e4m3fn", "e8m0_block32", "f32")
+    b = fn(xs, f32, "e4m3fn", "f32_group128", "f32")
+    ref = reduce_scatter_share(xs, f32, "e4m3fn", "f32_group128", "f32")
+    return np.array_equal(a.view(np.uint32), b.view(np.uint32)) and np.array_equal(b.view(np.uint32), ref.view(np.uint32))
+
+
+def _decode_pin_passes(table_fn, fmt, tdt):
+    want = torch.arange(256, dtype=torch.uint8).view(tdt).float().numpy()
+    got = table_fn(fmt)
+    ok = ~np.isnan(want)
+    return np.array_equal(np.isnan(got), ~ok) and np.array_equal(got[ok], want[ok])
+
+
+MUTANTS = {
+    "reverse_rank_order": dict(order=lambda n: list(range(n))[::-1]),
+    "pairwise_tree_sum": dict(pairwise=True),
+    "fp64_accumulate_like_fma": dict(wide=True),
+    "accumulator_starts_at_plus_zero": dict(start_zero=True),
+    "bf16_by_truncation": dict(to_bf16=_truncate_bf16),
+    "group_of_64_columns": dict(group=64),
+}
+
+
+def test_unmutated_restatement_passes():
+    fn = lambda *a: _fold(*a)  # noqa: E731
+    assert _worked_examples_pass(fn)
+    assert _cross_layout_passes(fn)
+    assert _worked_examples_pass(reduce_scatter_share)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    kw = MUTANTS[name]
+    fn = lambda *a: _fold(*a, **kw)  # noqa: E731
+    caught = (not _worked_examples_pass(fn)) or (not _cross_layout_passes(fn))
+    assert caught, f"no pin rejects the planted mistake {name}"
+
+
+def test_planted_decode_mistakes_are_caught():
+    def e5m2_bias16(fmt):
+        t = decode_table(fmt).astype(np.float64)
+        return np.where(np.isfinite(t), t / 2, t).astype(np.float32)
+
+    def e4m3_no_subnormals(fmt):
+        t = decode_table(fmt).copy()
+        t[1:8] = 0.0
+        t[0x81:0x88] = -0.0
+        return t
+
+    def int8_unsigned(fmt):
+        return np.arange(256, dtype=np.float32)
+
+    assert _decode_pin_passes(decode_table, "e5m2", torch.float8_e5m2)
+    assert not _decode_pin_passes(e5m2_bias16, "e5m2", torch.float8_e5m2)
+    assert not _decode_pin_passes(e4m3_no_subnormals, "e4m3fn", torch.float8_e4m3fn)
+    assert not _decode_pin_passes(int8_unsigned, "int8", torch.int8)
