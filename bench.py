@@ -1,0 +1,247 @@
+"""Benchmark: achieved HBM bandwidth of one GPU's share of the quantized
+reduce-scatter (dequant + rank-ordered reduce) on MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload C4] [--gpus 1]
+
+A step is one launch of the whole hot path (decode, scale, rank-ordered fp32
+fold, convert, store) over one batch: W rank slices of the workload, already
+resident in HBM. Several identical input/output sets are allocated and the
+steps rotate through them, so the working set of consecutive steps (well over
+the 256 MB Infinity Cache) is not served from that cache.
+
+Prints ONE JSON line on stdout:
+  value            whole-job throughput: algorithmic bytes x K / wall time of
+                   the K timed steps (GB/s);
+  roofline         for the reduce kernel: algorithmic bytes per launch /
+                   average launch duration (HIP events recorded on the launch
+                   stream at both ends of the K timed launches, divided by
+                   K), against the 8 TB/s HBM peak;
+                   traffic = measured HBM bytes per launch from committed
+                   rocprofv3 counter summaries, when they match this kernel
+                   source (else null);
+  cpu_baseline     the CPU oracle timed on the host (single thread) on the
+                   same workload.
+Diagnostics go to stderr.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
+METRIC = "achieved HBM GB/s and % of peak for dequant+reduce at W=8, H=8192"
+KERNEL_SOURCES = ("quantized_collective_reduction_amd/csrc/qrs_kernels.hip",)
+MALL_BYTES = 256 << 20
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def read_traffic(workload_name):
+    """HBM bytes per launch from profiles/traffic_<workload>.txt, if that
+    summary was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_reduce_{workload_name}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != kernel_source_digest():
+        log(f"[bench] {path} was taken on another kernel source: traffic = null")
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, xs, ss, min_seconds=10.0, min_reps=3):
+    """Time the oracle (as it stands) on the host, single-threaded."""
+    import oracle
+
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < min_reps or time.perf_counter() - t_start < min_seconds:
+        t0 = time.perf_counter()
+        oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 50:
+            break
+    med = statistics.median(times)
+    return {
+        "value": round(wl.algorithmic_bytes() / med / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"whole {wl.name} share ({wl.rows}x{wl.h} outputs from {wl.world_size} rank slices), "
+                  f"median of {len(times)} runs, {med:.3f} s each, numpy single thread",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="C4", help="C1..C5 (default C4: W=8, H=8192, the metric's workload)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (cpu_baseline = null)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share on one GPU only: run it with --gpus 1 "
+              "(the all-to-all between GPUs is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps <= 0 or args.warmup < 0:
+        sys.exit("--steps must be positive and --warmup non-negative")
+
+    import torch
+
+    import quantized_collective_reduction_amd as qrs
+    import workloads
+
+    qrs.load_library()
+    if not torch.cuda.is_available():
+        sys.exit("no GPU visible")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = workloads.CONFIGS[args.workload]
+    alg_bytes = wl.algorithmic_bytes()
+    log(f"[bench] {wl.name}: W={wl.world_size} BS={wl.bs} H={wl.h} rows={wl.rows} "
+        f"{wl.x_format}/{wl.scale_layout}->{wl.out_dtype}, {alg_bytes} algorithmic bytes per step")
+
+    t0 = time.perf_counter()
+    xs, ss = workloads.generate(wl)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    # Rotating sets: enough that consecutive steps touch over 4x the Infinity Cache.
+    n_sets = max(2, -(-4 * MALL_BYTES // alg_bytes))
+    out_dt = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
+    dx0 = [torch.from_numpy(x).to(dev) for x in xs]
+    ds0 = [torch.from_numpy(s).to(dev) for s in ss]
+    sets = []
+    for k in range(n_sets):
+        dx = dx0 if k == 0 else [t.clone() for t in dx0]
+        ds = ds0 if k == 0 else [t.clone() for t in ds0]
+        out = torch.empty((wl.rows, wl.h), dtype=out_dt, device=dev)
+        sets.append((dx, ds, out))
+    p = qrs.plan(wl.world_size, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    stream = torch.cuda.current_stream(dev)
+    launches = [qrs.Launch(p, dx, ds, out, stream=stream) for dx, ds, out in sets]
+    torch.cuda.synchronize()
+    log(f"[bench] {n_sets} rotating input/output sets on {torch.cuda.get_device_name(dev)}")
+
+    for i in range(args.warmup):
+        launches[i % n_sets]()
+    torch.cuda.synchronize()
+    # All sets hold identical inputs, so every set must produce the same bits.
+    if args.warmup >= n_sets:
+        ref = sets[0][2].view(torch.uint8)
+        for _, _, out in sets[1:]:
+            if not torch.equal(out.view(torch.uint8), ref):
+                sys.exit("rotating sets disagree: the kernel is not deterministic")
+
+    # Timed region: K back-to-back launches, HIP events on the launch stream
+    # at both ends, wall clock around it.
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    order = [launches[(args.warmup + i) % n_sets] for i in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for launch in order:
+        launch()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+    log(f"[bench] {args.steps} steps in {wall * 1e3:.2f} ms wall; HIP events over the region: "
+        f"{avg_launch_s * 1e6:.2f} us per launch")
+
+    # Calibration: the plain 16-byte stream copy of the same read+write volume.
+    copy_bytes = (alg_bytes // 2) // 16 * 16
+    src = torch.empty(copy_bytes * n_sets, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    c_starts = [torch.cuda.Event(enable_timing=True) for _ in range(50)]
+    c_ends = [torch.cuda.Event(enable_timing=True) for _ in range(50)]
+    for i in range(60):
+        k = i % n_sets
+        j = i - 10
+        if j >= 0:
+            c_starts[j].record(stream)
+        qrs.stream_copy(src[k * copy_bytes:(k + 1) * copy_bytes], dst[k * copy_bytes:(k + 1) * copy_bytes],
+                        stream=stream)
+        if j >= 0:
+            c_ends[j].record(stream)
+    torch.cuda.synchronize()
+    copy_s = statistics.fmean(s.elapsed_time(e) for s, e in zip(c_starts, c_ends)) / 1e3
+    copy_gbps = 2 * copy_bytes / copy_s / 1e9
+    log(f"[bench] stream-copy calibration: {2 * copy_bytes} bytes moved in {copy_s * 1e6:.2f} us = {copy_gbps:.0f} GB/s")
+    del src, dst
+
+    achieved = alg_bytes / avg_launch_s / 1e9
+    value = alg_bytes * args.steps / wall / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: W={wl.world_size} BS={wl.bs} H={wl.h} x={wl.x_format} "
+                        f"scales={wl.scale_layout} out={wl.out_dtype}",
+            "world_size": wl.world_size,
+            "bs": wl.bs,
+            "rows": wl.rows,
+            "h": wl.h,
+            "algorithmic_bytes_per_step": alg_bytes,
+            "rotating_sets": n_sets,
+        },
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": read_traffic(wl.name),
+            "kernel_us_avg": round(avg_launch_s * 1e6, 3),
+        },
+        "copy_calibration": {"bytes_moved": 2 * copy_bytes, "GBps": round(copy_gbps, 1)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(wl, xs, ss)
+        log(f"[bench] cpu baseline: {result['cpu_baseline']}")
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,158 @@
+/*
+ * qrs.h -- C ABI for one GPU's share of a quantized reduce-scatter on MI355X
+ * (gfx950).
+ *
+ * The operation (page "aclnnQuantReduceScatter", Function description): the
+ * output is a reduction, over the data arriving from the different ranks, of
+ * the all-to-all'ed scales multiplied by the all-to-all'ed quantized x. On
+ * one GPU the all-to-all has already happened: the caller passes W rank
+ * slices of x codes, each [rows, H] with rows = BS / W, and their scales.
+ * For every row i and column c, with G the group size of the scale layout:
+ *
+ *     p_r      = fp32( decode(x_r[i][c]) * decode(scale_r[i][c / G]) )
+ *     acc      = p_0;  acc = fp32(acc + p_r)  for r = 1 .. W-1, in rank order
+ *     out[i][c] = acc                 (QRS_OUT_F32)
+ *     out[i][c] = bf16_rne(acc)       (QRS_OUT_BF16)
+ *
+ * Products and sums are separate binary32 operations rounded to nearest-even
+ * (no fused multiply-add), subnormals are kept, NaN and infinity propagate.
+ * The fixed rank order makes the result deterministic.
+ *
+ * The calls follow the page's two-phase form (Prototype): a first call
+ * checks the parameters and prepares the computation (qrs_plan, host only),
+ * a second runs it on a stream (qrs_run). Both return a status code. The
+ * parameter and error tables of the page did not survive, so names and codes
+ * here are this library's own.
+ *
+ * Ownership: the caller owns every device buffer and the stream; the library
+ * owns only the plan. No call allocates device memory; the workspace size is
+ * always 0. A plan is immutable and may be used by any number of concurrent
+ * qrs_run calls on different streams.
+ *
+ * Errors: every call returns a qrs_status. On failure, qrs_last_error()
+ * returns a human-readable message for the calling thread.
+ */
+#ifndef QRS_H_
+#define QRS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qrs_status {
+  QRS_OK = 0,
+  QRS_ERR_INVALID_ARG = 1, /* a parameter breaks a documented constraint   */
+  QRS_ERR_UNSUPPORTED = 2, /* a format the library does not implement      */
+  QRS_ERR_HIP = 3          /* the HIP runtime reported an error at launch  */
+} qrs_status;
+
+/* Element format of x (page "aclnnQuantReduceScatter", Constraints).
+ * FP8 formats are the OCP 8-bit float formats. HIFLOAT8 is listed by the page
+ * but never defined there, so it is reserved and always rejected with
+ * QRS_ERR_UNSUPPORTED. */
+typedef enum qrs_x_dtype {
+  QRS_X_INT8 = 0,       /* two's complement byte                         */
+  QRS_X_FP8_E4M3FN = 1, /* OCP E4M3 "FN": bias 7, no inf, max 448        */
+  QRS_X_FP8_E5M2 = 2,   /* OCP E5M2: bias 15, inf/NaN, max 57344         */
+  QRS_X_HIFLOAT8 = 3    /* reserved                                      */
+} qrs_x_dtype;
+
+/* Scale layout (same page, Constraints). Groups and blocks run along H
+ * within one token, so slice r's scales are row-major:
+ *   QRS_SCALE_F32_GROUP128: float32 [rows, H/128], per-token-per-group mode,
+ *                           for INT8, E4M3FN or E5M2 x;
+ *   QRS_SCALE_E8M0_BLOCK32: uint8 E8M0 [rows, H/32] (value 2^(code-127),
+ *                           code 255 = NaN), MX mode, for E4M3FN or E5M2 x.
+ * The block of 32 is fixed by the page's MX scales size (one byte per 32
+ * elements of x). */
+typedef enum qrs_scale_layout {
+  QRS_SCALE_F32_GROUP128 = 0,
+  QRS_SCALE_E8M0_BLOCK32 = 1
+} qrs_scale_layout;
+
+typedef enum qrs_out_dtype {
+  QRS_OUT_F32 = 0, /* float32 [rows, H]                                 */
+  QRS_OUT_BF16 = 1 /* bfloat16 [rows, H], round-to-nearest-even of fp32 */
+} qrs_out_dtype;
+
+typedef struct qrs_plan_s* qrs_plan_t;
+
+/*
+ * Phase 1: check the problem and prepare a plan. Host only, no GPU work.
+ *
+ *   world_size  W, the communicator size: 2, 4 or 8 (Constraints).
+ *   bs          tokens per rank before the all-to-all (x is [BS, H] on each
+ *               rank, Constraints); must be > 0 (no empty input) and a
+ *               multiple of W. This GPU's share has rows = bs / W.
+ *   h           hidden size: a multiple of 128 in [1024, 8192] (Constraints).
+ *   x_dtype, scale_layout, out_dtype
+ *               a pair that selects a mode of the page: MX needs an FP8 x;
+ *               INT8 with E8M0 is QRS_ERR_INVALID_ARG; HIFLOAT8 is
+ *               QRS_ERR_UNSUPPORTED.
+ *   plan_out    receives the plan (non-null). Free it with qrs_plan_destroy.
+ *   workspace_bytes_out
+ *               receives the device workspace size, always 0 (non-null).
+ *
+ * Returns QRS_OK, QRS_ERR_INVALID_ARG or QRS_ERR_UNSUPPORTED. On error
+ * *plan_out is set to NULL (when plan_out is non-null).
+ */
+qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, qrs_scale_layout scale_layout,
+                    qrs_out_dtype out_dtype, qrs_plan_t* plan_out, size_t* workspace_bytes_out);
+
+/*
+ * Phase 2: run the planned share on a stream. Asynchronous: no host
+ * synchronisation, no allocation.
+ *
+ *   x_slices      HOST array of W DEVICE pointers; x_slices[r] is rank r's
+ *                 uint8 codes [rows, H], contiguous row-major, 16-byte
+ *                 aligned. One [W, rows, H] buffer is the case of equally
+ *                 spaced pointers.
+ *   scale_slices  HOST array of W DEVICE pointers to rank r's scales in the
+ *                 plan's layout, contiguous row-major; fp32 scales 4-byte
+ *                 aligned.
+ *   out           DEVICE buffer [rows, H] of the plan's output type, 16-byte
+ *                 aligned, not overlapping any input.
+ *   workspace, workspace_bytes
+ *                 unused (the plan needs none); any value is accepted.
+ *   stream        a hipStream_t (NULL = the default stream).
+ *
+ * Returns QRS_ERR_INVALID_ARG for a null plan or pointer, a misaligned
+ * pointer or an output that overlaps an input, and QRS_ERR_HIP if the kernel
+ * launch fails. Inputs are not validated element by element: NaN or
+ * infinite codes and scales propagate as in IEEE 754.
+ */
+qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* const* scale_slices, void* out,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Free a plan. NULL is accepted. Plans in use by queued runs may be freed:
+ * qrs_run copies what the kernel needs into its launch arguments. */
+qrs_status qrs_plan_destroy(qrs_plan_t plan);
+
+/* Shape of a plan's share: rows = bs / world_size and h. Either out-pointer
+ * may be NULL. */
+qrs_status qrs_plan_shape(qrs_plan_t plan, int64_t* rows_out, int64_t* h_out);
+
+/* Static, never-null name of a status code. */
+const char* qrs_status_string(qrs_status status);
+
+/* Message describing the calling thread's most recent failing call (empty
+ * if none). Valid until that thread's next call into the library. */
+const char* qrs_last_error(void);
+
+/*
+ * Utility, not part of the operation: copy `bytes` bytes from src to dst on
+ * `stream` with the same 16-byte streaming loads and stores the reduction
+ * uses. It is the reference stream for bandwidth and traffic-counter
+ * calibration. bytes must be a positive multiple of 16, both pointers
+ * 16-byte aligned device pointers, and the ranges must not overlap.
+ */
+qrs_status qrs_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QRS_H_ */

@@ -1,0 +1,250 @@
+"""Python binding for libqrs: one GPU's share of a quantized reduce-scatter
+on MI355X.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/qrs.h). torch supplies device memory and
+streams. If the built library is missing, loading fails with an error; there
+is no CPU fallback.
+
+    p = plan(world_size=8, bs=16384, h=8192, x_dtype="e4m3fn",
+             scale_layout="e8m0_block32", out_dtype="bf16")
+    run(p, x_slices, scale_slices, out)        # on torch's current stream
+
+``x_slices`` / ``scale_slices`` are sequences of W device tensors (or raw
+device pointers as ints); ``out`` is a ``[rows, H]`` device tensor.
+"""
+
+import ctypes
+import os
+from enum import IntEnum
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libqrs.so")
+
+__all__ = [
+    "Status",
+    "XDtype",
+    "ScaleLayout",
+    "OutDtype",
+    "QrsError",
+    "Plan",
+    "load_library",
+    "plan",
+    "run",
+    "Launch",
+    "stream_copy",
+    "EXPORTED_SYMBOLS",
+]
+
+
+class Status(IntEnum):
+    OK = 0
+    INVALID_ARG = 1
+    UNSUPPORTED = 2
+    HIP = 3
+
+
+class XDtype(IntEnum):
+    INT8 = 0
+    FP8_E4M3FN = 1
+    FP8_E5M2 = 2
+    HIFLOAT8 = 3
+
+
+class ScaleLayout(IntEnum):
+    F32_GROUP128 = 0
+    E8M0_BLOCK32 = 1
+
+
+class OutDtype(IntEnum):
+    F32 = 0
+    BF16 = 1
+
+
+_X_NAMES = {"int8": XDtype.INT8, "e4m3fn": XDtype.FP8_E4M3FN, "e5m2": XDtype.FP8_E5M2, "hifloat8": XDtype.HIFLOAT8}
+_SCALE_NAMES = {"f32_group128": ScaleLayout.F32_GROUP128, "e8m0_block32": ScaleLayout.E8M0_BLOCK32}
+_OUT_NAMES = {"f32": OutDtype.F32, "bf16": OutDtype.BF16}
+
+# Every function include/qrs.h declares.
+EXPORTED_SYMBOLS = (
+    "qrs_plan",
+    "qrs_run",
+    "qrs_plan_destroy",
+    "qrs_plan_shape",
+    "qrs_status_string",
+    "qrs_last_error",
+    "qrs_stream_copy",
+)
+
+
+class QrsError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = Status(status)
+        super().__init__(f"{self.status.name}: {message}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libqrs.so and declare its signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m quantized_collective_reduction_amd._build` "
+            "(there is no CPU fallback)"
+        )
+    lib = ctypes.CDLL(path)
+    c_int, c_i64, c_sz, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    lib.qrs_plan.argtypes = [c_int, c_i64, c_i64, c_int, c_int, c_int, ctypes.POINTER(vp), ctypes.POINTER(c_sz)]
+    lib.qrs_plan.restype = c_int
+    lib.qrs_run.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, c_sz, vp]
+    lib.qrs_run.restype = c_int
+    lib.qrs_plan_destroy.argtypes = [vp]
+    lib.qrs_plan_destroy.restype = c_int
+    lib.qrs_plan_shape.argtypes = [vp, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]
+    lib.qrs_plan_shape.restype = c_int
+    lib.qrs_status_string.argtypes = [c_int]
+    lib.qrs_status_string.restype = ctypes.c_char_p
+    lib.qrs_last_error.argtypes = []
+    lib.qrs_last_error.restype = ctypes.c_char_p
+    lib.qrs_stream_copy.argtypes = [vp, vp, c_sz, vp]
+    lib.qrs_stream_copy.restype = c_int
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != Status.OK:
+        msg = _lib.qrs_last_error().decode(errors="replace")
+        raise QrsError(status, msg)
+
+
+def _enum(value, names, enum_cls):
+    if isinstance(value, str):
+        return names[value.lower()]
+    return enum_cls(value) if value in enum_cls._value2member_map_ else int(value)
+
+
+class Plan:
+    """An immutable plan for one share shape and mode (phase 1 of the op)."""
+
+    def __init__(self, world_size, bs, h, x_dtype, scale_layout, out_dtype):
+        lib = load_library()
+        self.world_size = int(world_size)
+        self.bs = int(bs)
+        self.h = int(h)
+        self.x_dtype = _enum(x_dtype, _X_NAMES, XDtype)
+        self.scale_layout = _enum(scale_layout, _SCALE_NAMES, ScaleLayout)
+        self.out_dtype = _enum(out_dtype, _OUT_NAMES, OutDtype)
+        handle = ctypes.c_void_p()
+        ws = ctypes.c_size_t()
+        self._handle = None
+        _check(lib.qrs_plan(self.world_size, self.bs, self.h, int(self.x_dtype), int(self.scale_layout),
+                            int(self.out_dtype), ctypes.byref(handle), ctypes.byref(ws)))
+        self._handle = handle
+        self.workspace_bytes = ws.value
+        rows, hh = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.qrs_plan_shape(handle, ctypes.byref(rows), ctypes.byref(hh)))
+        self.rows = rows.value
+
+    @property
+    def handle(self):
+        return self._handle
+
+    @property
+    def group(self):
+        return 128 if self.scale_layout == ScaleLayout.F32_GROUP128 else 32
+
+    def __del__(self):
+        if self._handle is not None and _lib is not None:
+            _lib.qrs_plan_destroy(self._handle)
+            self._handle = None
+
+
+def plan(world_size, bs, h, x_dtype, scale_layout, out_dtype) -> Plan:
+    return Plan(world_size, bs, h, x_dtype, scale_layout, out_dtype)
+
+
+def _ptr(t):
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("device tensors only (there is no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_handle(stream):
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check_tensor(t, nbytes, what):
+    if isinstance(t, int):
+        return
+    if t.numel() * t.element_size() != nbytes:
+        raise ValueError(f"{what}: expected {nbytes} bytes, got {t.numel() * t.element_size()}")
+
+
+def run(p: Plan, x_slices, scale_slices, out, stream=None):
+    """Phase 2: enqueue the share on ``stream`` (torch's current stream by default)."""
+    lib = load_library()
+    w = p.world_size
+    if len(x_slices) != w or len(scale_slices) != w:
+        raise ValueError(f"need {w} x slices and {w} scale slices")
+    n = p.rows * p.h
+    scale_bytes = n // 128 * 4 if p.scale_layout == ScaleLayout.F32_GROUP128 else n // 32
+    for r in range(w):
+        _check_tensor(x_slices[r], n, f"x slice {r}")
+        _check_tensor(scale_slices[r], scale_bytes, f"scale slice {r}")
+    _check_tensor(out, n * (4 if p.out_dtype == OutDtype.F32 else 2), "out")
+    xs = (ctypes.c_void_p * w)(*[_ptr(t) for t in x_slices])
+    ss = (ctypes.c_void_p * w)(*[_ptr(t) for t in scale_slices])
+    _check(lib.qrs_run(p.handle, xs, ss, _ptr(out), None, 0, _stream_handle(stream)))
+
+
+class Launch:
+    """Arguments for ``run`` marshalled once, for repeated launches of one
+    plan on fixed buffers (each call is a single C call: no per-call Python
+    checks or array building)."""
+
+    def __init__(self, p: Plan, x_slices, scale_slices, out, stream=None):
+        lib = load_library()
+        w = p.world_size
+        if len(x_slices) != w or len(scale_slices) != w:
+            raise ValueError(f"need {w} x slices and {w} scale slices")
+        n = p.rows * p.h
+        scale_bytes = n // 128 * 4 if p.scale_layout == ScaleLayout.F32_GROUP128 else n // 32
+        for r in range(w):
+            _check_tensor(x_slices[r], n, f"x slice {r}")
+            _check_tensor(scale_slices[r], scale_bytes, f"scale slice {r}")
+        _check_tensor(out, n * (4 if p.out_dtype == OutDtype.F32 else 2), "out")
+        self._plan = p  # keeps the plan alive
+        self._keep = (list(x_slices), list(scale_slices), out)  # keeps the buffers alive
+        self._xs = (ctypes.c_void_p * w)(*[_ptr(t) for t in x_slices])
+        self._ss = (ctypes.c_void_p * w)(*[_ptr(t) for t in scale_slices])
+        self._out = ctypes.c_void_p(_ptr(out))
+        self._stream = ctypes.c_void_p(_stream_handle(stream))
+        self._fn = lib.qrs_run
+        self._handle = p.handle
+
+    def __call__(self):
+        status = self._fn(self._handle, self._xs, self._ss, self._out, None, 0, self._stream)
+        if status:
+            _check(status)
+
+
+def stream_copy(src, dst, nbytes=None, stream=None):
+    """Calibration copy of ``nbytes`` (default: all of src) from src to dst."""
+    lib = load_library()
+    if nbytes is None:
+        nbytes = src.numel() * src.element_size()
+    _check(lib.qrs_stream_copy(_ptr(src), _ptr(dst), int(nbytes), _stream_handle(stream)))

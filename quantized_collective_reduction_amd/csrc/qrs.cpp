@@ -1,0 +1,168 @@
+// C-ABI host library: parameter checks, plans, and launches on the caller's
+// stream. The contract of every entry point is documented in include/qrs.h.
+
+#include "qrs.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+
+#include "qrs_launch.h"
+
+struct qrs_plan_s {
+  int world_size;
+  int64_t bs;
+  int64_t rows;
+  int64_t h;
+  qrs::XFormat x_format;
+  qrs::ScaleLayout scale_layout;
+  qrs::OutFormat out_format;
+};
+
+namespace {
+
+thread_local char g_last_error[512];
+
+qrs_status fail(qrs_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+qrs_status ok() {
+  g_last_error[0] = '\0';
+  return QRS_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qrs_status_string(qrs_status status) {
+  switch (status) {
+    case QRS_OK: return "QRS_OK";
+    case QRS_ERR_INVALID_ARG: return "QRS_ERR_INVALID_ARG";
+    case QRS_ERR_UNSUPPORTED: return "QRS_ERR_UNSUPPORTED";
+    case QRS_ERR_HIP: return "QRS_ERR_HIP";
+  }
+  return "QRS_ERR_UNKNOWN";
+}
+
+const char* qrs_last_error(void) { return g_last_error; }
+
+qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, qrs_scale_layout scale_layout,
+                    qrs_out_dtype out_dtype, qrs_plan_t* plan_out, size_t* workspace_bytes_out) {
+  if (plan_out) *plan_out = nullptr;
+  if (!plan_out || !workspace_bytes_out) return fail(QRS_ERR_INVALID_ARG, "plan_out and workspace_bytes_out must be non-null");
+  // Communicator size 2, 4 or 8.
+  if (world_size != 2 && world_size != 4 && world_size != 8)
+    return fail(QRS_ERR_INVALID_ARG, "world_size %d: must be 2, 4 or 8", world_size);
+  // Empty input is not supported; the share has bs / W rows.
+  if (bs <= 0) return fail(QRS_ERR_INVALID_ARG, "bs %lld: must be positive", static_cast<long long>(bs));
+  if (bs % world_size != 0)
+    return fail(QRS_ERR_INVALID_ARG, "bs %lld is not a multiple of world_size %d", static_cast<long long>(bs),
+                world_size);
+  // H is 128-aligned and in [1024, 8192].
+  if (h < 1024 || h > 8192 || h % 128 != 0)
+    return fail(QRS_ERR_INVALID_ARG, "h %lld: must be a multiple of 128 in [1024, 8192]", static_cast<long long>(h));
+  const int64_t rows = bs / world_size;
+  // rows * h elements, each a 16-element chunk per lane; keep the launch in range.
+  if (rows > (int64_t{1} << 40) / h) return fail(QRS_ERR_INVALID_ARG, "bs %lld too large", static_cast<long long>(bs));
+
+  if (x_dtype == QRS_X_HIFLOAT8)
+    return fail(QRS_ERR_UNSUPPORTED, "HIFLOAT8 x is reserved: its encoding is not defined");
+  if (x_dtype != QRS_X_INT8 && x_dtype != QRS_X_FP8_E4M3FN && x_dtype != QRS_X_FP8_E5M2)
+    return fail(QRS_ERR_INVALID_ARG, "x_dtype %d is not a qrs_x_dtype", static_cast<int>(x_dtype));
+  if (scale_layout != QRS_SCALE_F32_GROUP128 && scale_layout != QRS_SCALE_E8M0_BLOCK32)
+    return fail(QRS_ERR_INVALID_ARG, "scale_layout %d is not a qrs_scale_layout", static_cast<int>(scale_layout));
+  // MX mode (E8M0 scales) is defined for the FP8 formats only.
+  if (scale_layout == QRS_SCALE_E8M0_BLOCK32 && x_dtype == QRS_X_INT8)
+    return fail(QRS_ERR_INVALID_ARG, "INT8 x is paired with fp32 per-group scales only");
+  if (out_dtype != QRS_OUT_F32 && out_dtype != QRS_OUT_BF16)
+    return fail(QRS_ERR_INVALID_ARG, "out_dtype %d is not a qrs_out_dtype", static_cast<int>(out_dtype));
+
+  qrs_plan_s* p = new (std::nothrow) qrs_plan_s;
+  if (!p) return fail(QRS_ERR_INVALID_ARG, "out of host memory");
+  p->world_size = world_size;
+  p->bs = bs;
+  p->rows = rows;
+  p->h = h;
+  p->x_format = x_dtype == QRS_X_INT8 ? qrs::kXInt8 : x_dtype == QRS_X_FP8_E4M3FN ? qrs::kXE4M3FN : qrs::kXE5M2;
+  p->scale_layout = scale_layout == QRS_SCALE_F32_GROUP128 ? qrs::kScaleF32Group128 : qrs::kScaleE8M0Block32;
+  p->out_format = out_dtype == QRS_OUT_F32 ? qrs::kOutF32 : qrs::kOutBF16;
+  *plan_out = p;
+  *workspace_bytes_out = 0;
+  return ok();
+}
+
+qrs_status qrs_plan_destroy(qrs_plan_t plan) {
+  delete plan;
+  return ok();
+}
+
+qrs_status qrs_plan_shape(qrs_plan_t plan, int64_t* rows_out, int64_t* h_out) {
+  if (!plan) return fail(QRS_ERR_INVALID_ARG, "null plan");
+  if (rows_out) *rows_out = plan->rows;
+  if (h_out) *h_out = plan->h;
+  return ok();
+}
+
+qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* const* scale_slices, void* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!plan) return fail(QRS_ERR_INVALID_ARG, "null plan");
+  if (!x_slices || !scale_slices || !out) return fail(QRS_ERR_INVALID_ARG, "null pointer array or output");
+  const int W = plan->world_size;
+  const uint64_t n = static_cast<uint64_t>(plan->rows) * static_cast<uint64_t>(plan->h);
+  const bool f32_scales = plan->scale_layout == qrs::kScaleF32Group128;
+  const uint64_t scale_bytes = f32_scales ? n / 128 * 4 : n / 32;
+  const uint64_t out_bytes = n * (plan->out_format == qrs::kOutF32 ? 4 : 2);
+  if (!aligned(out, 16)) return fail(QRS_ERR_INVALID_ARG, "out is not 16-byte aligned");
+
+  qrs::ReduceLaunch l;
+  std::memset(&l, 0, sizeof(l));
+  l.world_size = W;
+  l.x_format = plan->x_format;
+  l.scale_layout = plan->scale_layout;
+  l.out_format = plan->out_format;
+  l.n_elems = n;
+  l.out = out;
+  for (int r = 0; r < W; ++r) {
+    if (!x_slices[r] || !scale_slices[r]) return fail(QRS_ERR_INVALID_ARG, "null slice pointer for rank %d", r);
+    if (!aligned(x_slices[r], 16)) return fail(QRS_ERR_INVALID_ARG, "x slice of rank %d is not 16-byte aligned", r);
+    if (f32_scales && !aligned(scale_slices[r], 4))
+      return fail(QRS_ERR_INVALID_ARG, "fp32 scale slice of rank %d is not 4-byte aligned", r);
+    if (overlaps(out, out_bytes, x_slices[r], n) || overlaps(out, out_bytes, scale_slices[r], scale_bytes))
+      return fail(QRS_ERR_INVALID_ARG, "out overlaps an input slice of rank %d", r);
+    l.x[r] = x_slices[r];
+    l.scales[r] = scale_slices[r];
+  }
+  const hipError_t e = qrs::launch_reduce(l, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qrs_status qrs_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (!src || !dst) return fail(QRS_ERR_INVALID_ARG, "null pointer");
+  if (bytes == 0 || bytes % 16 != 0) return fail(QRS_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (!aligned(src, 16) || !aligned(dst, 16)) return fail(QRS_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
+  if (overlaps(src, bytes, dst, bytes)) return fail(QRS_ERR_INVALID_ARG, "ranges overlap");
+  const hipError_t e = qrs::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

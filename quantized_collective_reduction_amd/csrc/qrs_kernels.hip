@@ -1,0 +1,348 @@
+// gfx950 kernels for one GPU's share of the quantized reduce-scatter.
+//
+// Page "aclnnQuantReduceScatter", Function description: the output is the
+// reduction, over the data of the different ranks, of the exchanged scales
+// times the exchanged quantized x. Here the exchange has already happened:
+// W rank slices [rows, H] of x codes and their scales sit in HBM, and each
+// output element is
+//
+//   p_r = fp32(decode(x_r) * decode(scale_r))      one rounding
+//   acc = p_0, then acc = fp32(acc + p_r) for r = 1 .. W-1, in rank order
+//   out = acc (fp32) or round-to-nearest-even(acc) (bf16)
+//
+// Modes (same page, Constraints): FP8 E4M3FN / E5M2 x with one E8M0 scale per
+// 32 elements (MX), or INT8 / E4M3FN / E5M2 x with one fp32 scale per token
+// and 128-column group.
+//
+// The work is a read-once stream with no reuse, so it is bound by HBM, not by
+// arithmetic: no matrix cores. Each lane owns 16 consecutive elements of the
+// flat [rows*H] range (a "chunk"). It issues one 16-byte load per rank for
+// the codes plus one scale load per rank, decodes with the CDNA4 fp8/bf8
+// conversion instructions (two elements per instruction), multiplies and
+// adds in separate fp32 instructions (no contraction, so results match the
+// definition bit for bit), converts with the packed bf16 round-to-nearest-
+// even instruction, and writes 16-byte stores. All W loads are issued before
+// any arithmetic, so each lane has W*16 bytes in flight.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qrs_launch.h"
+
+// The definition has one rounding per product and per sum: never fuse.
+#pragma clang fp contract(off)
+
+#ifndef QRS_BLOCK
+#define QRS_BLOCK 256
+#endif
+// Chunks of 16 elements per lane.
+#ifndef QRS_CHUNKS_PER_LANE
+#define QRS_CHUNKS_PER_LANE 1
+#endif
+// Streaming (non-temporal) hint on the x loads, read exactly once.
+#ifndef QRS_NT_LOADS
+#define QRS_NT_LOADS 1
+#endif
+// Streaming hint on the output stores, written exactly once.
+#ifndef QRS_NT_STORES
+#define QRS_NT_STORES 1
+#endif
+// Route each wave's output through LDS so that every store instruction of
+// the wave writes one contiguous 1 KiB range. A lane's own 16 results are 64
+// contiguous bytes in fp32, so without staging each store instruction writes
+// 16 bytes every 64, and streaming stores of that shape run at half the
+// bandwidth. In bf16 (32 bytes per lane) direct stores measured faster.
+// 0: never stage, 1: stage fp32 output only, 2: always stage.
+#ifndef QRS_STAGE_STORES
+#define QRS_STAGE_STORES 1
+#endif
+// 1: block barrier around the LDS exchange; 0: wave-local ordering only.
+#ifndef QRS_STAGE_BLOCK_SYNC
+#define QRS_STAGE_BLOCK_SYNC 0
+#endif
+
+namespace qrs {
+namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kChunk = 16;  // elements per chunk: one 16-byte load of codes
+
+template <typename T>
+__device__ __forceinline__ T load_stream(const T* p) {
+#if QRS_NT_LOADS
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+template <typename T>
+__device__ __forceinline__ void store_stream(T* p, T v) {
+#if QRS_NT_STORES
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+// Decode two adjacent codes of a 32-bit word: bytes 0,1 (hi == false) or
+// bytes 2,3 (hi == true). Every code maps exactly to an fp32 value; the fp8
+// conversions are the gfx950 OCP E4M3 / E5M2 ones.
+template <int XF>
+__device__ __forceinline__ f32x2 decode_pair(uint32_t w, bool hi);
+
+template <>
+__device__ __forceinline__ f32x2 decode_pair<kXE4M3FN>(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_pk_f32_fp8(w, true) : __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+}
+
+template <>
+__device__ __forceinline__ f32x2 decode_pair<kXE5M2>(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_pk_f32_bf8(w, true) : __builtin_amdgcn_cvt_pk_f32_bf8(w, false);
+}
+
+template <>
+__device__ __forceinline__ f32x2 decode_pair<kXInt8>(uint32_t w, bool hi) {
+  const uint32_t v = hi ? (w >> 16) : w;
+  f32x2 r;
+  r.x = static_cast<float>(static_cast<int8_t>(v & 0xFFu));
+  r.y = static_cast<float>(static_cast<int8_t>((v >> 8) & 0xFFu));
+  return r;
+}
+
+// E8M0 scale byte -> fp32: 2^(b-127). b = 0 is the fp32 subnormal 2^-127,
+// b = 255 is NaN; otherwise the byte is the fp32 exponent field.
+__device__ __forceinline__ float decode_e8m0(uint32_t b) {
+  uint32_t bits = b << 23;
+  bits = (b == 0u) ? 0x00400000u : bits;
+  bits = (b == 255u) ? 0x7FC00000u : bits;
+  return __builtin_bit_cast(float, bits);
+}
+
+template <int SL>
+__device__ __forceinline__ float load_scale(const void* base, uint64_t chunk) {
+  if constexpr (SL == kScaleF32Group128) {
+    // 128 elements = 8 chunks share one fp32 scale.
+    return static_cast<const float*>(base)[chunk >> 3];
+  } else {
+    // 32 elements = 2 chunks share one E8M0 byte.
+    return decode_e8m0(static_cast<const uint8_t*>(base)[chunk >> 1]);
+  }
+}
+
+struct KernelArgs {
+  const u32x4* x[kMaxWorld];
+  const void* scales[kMaxWorld];
+  void* out;
+  uint64_t n_chunks;
+};
+
+// Orders a wave's LDS writes before its following LDS reads of other lanes'
+// data (LDS instructions of one wave execute in order; this stops the
+// compiler from moving the reads above the writes).
+__device__ __forceinline__ void stage_sync() {
+#if QRS_STAGE_BLOCK_SYNC
+  __syncthreads();
+#else
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#endif
+}
+
+// acc[0..15] = rank-ordered fold of the dequantized products of one chunk.
+template <int W, int XF>
+__device__ __forceinline__ void fold_chunk(const u32x4 (&xv)[W], const float (&sv)[W], float (&acc)[kChunk]) {
+  // Rank 0 starts the fold: acc = p_0.
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t w = xv[0][q];
+    const f32x2 lo = decode_pair<XF>(w, false);
+    const f32x2 hi = decode_pair<XF>(w, true);
+    acc[4 * q + 0] = lo.x * sv[0];
+    acc[4 * q + 1] = lo.y * sv[0];
+    acc[4 * q + 2] = hi.x * sv[0];
+    acc[4 * q + 3] = hi.y * sv[0];
+  }
+  // Ranks 1..W-1 in order: acc = acc + p_r, each a separate rounding.
+#pragma unroll
+  for (int r = 1; r < W; ++r) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = xv[r][q];
+      const f32x2 lo = decode_pair<XF>(w, false);
+      const f32x2 hi = decode_pair<XF>(w, true);
+      const float p0 = lo.x * sv[r];
+      const float p1 = lo.y * sv[r];
+      const float p2 = hi.x * sv[r];
+      const float p3 = hi.y * sv[r];
+      acc[4 * q + 0] = acc[4 * q + 0] + p0;
+      acc[4 * q + 1] = acc[4 * q + 1] + p1;
+      acc[4 * q + 2] = acc[4 * q + 2] + p2;
+      acc[4 * q + 3] = acc[4 * q + 3] + p3;
+    }
+  }
+}
+
+// The chunk's output as 16-byte pieces: 4 for fp32, 2 for bf16.
+template <int OF>
+struct OutPieces {
+  static constexpr int kCount = OF == kOutF32 ? 4 : 2;
+};
+
+template <int OF>
+__device__ __forceinline__ void pack_chunk(const float (&acc)[kChunk], u32x4 (&piece)[OutPieces<OF>::kCount]) {
+  if constexpr (OF == kOutF32) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      piece[q] = u32x4{__builtin_bit_cast(uint32_t, acc[4 * q + 0]), __builtin_bit_cast(uint32_t, acc[4 * q + 1]),
+                       __builtin_bit_cast(uint32_t, acc[4 * q + 2]), __builtin_bit_cast(uint32_t, acc[4 * q + 3])};
+    }
+  } else {
+    uint32_t packed[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      f32x2 pr;
+      pr.x = acc[2 * k];
+      pr.y = acc[2 * k + 1];
+      // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN.
+      packed[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+    }
+    piece[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
+    piece[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
+  }
+}
+
+template <int W, int XF, int SL, int OF>
+__global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
+  constexpr int CH = QRS_CHUNKS_PER_LANE;
+  constexpr int P = OutPieces<OF>::kCount;
+  // Chunk j of this lane is base + j*QRS_BLOCK: every load instruction of a
+  // wave covers one contiguous range.
+  const uint64_t block_first = static_cast<uint64_t>(blockIdx.x) * (QRS_BLOCK * CH);
+  const uint64_t base = block_first + threadIdx.x;
+
+  u32x4 xv[CH][W];
+  float sv[CH][W];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const uint64_t c = base + static_cast<uint64_t>(j) * QRS_BLOCK;
+    if (c < a.n_chunks) {
+#pragma unroll
+      for (int r = 0; r < W; ++r) xv[j][r] = load_stream(a.x[r] + c);
+#pragma unroll
+      for (int r = 0; r < W; ++r) sv[j][r] = load_scale<SL>(a.scales[r], c);
+    }
+  }
+
+  u32x4* const out = static_cast<u32x4*>(a.out);
+  constexpr bool kStage = QRS_STAGE_STORES == 2 || (QRS_STAGE_STORES == 1 && OF == kOutF32);
+  __shared__ u32x4 stage[kStage ? QRS_BLOCK * P : 1];
+  [[maybe_unused]] const int lane = threadIdx.x & 63;
+  [[maybe_unused]] u32x4* const wave_stage = stage + (kStage ? (threadIdx.x & ~63) * P : 0);
+
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const uint64_t c = base + static_cast<uint64_t>(j) * QRS_BLOCK;
+    u32x4 piece[P];
+    if (c < a.n_chunks) {
+      float acc[kChunk];
+      fold_chunk<W, XF>(xv[j], sv[j], acc);
+      pack_chunk<OF>(acc, piece);
+      if constexpr (!kStage) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) store_stream(out + c * P + q, piece[q]);
+      }
+    }
+    if constexpr (kStage) {
+      // The wave's 64 chunks are contiguous in the output: write them to LDS
+      // in output order, then let lane l store pieces l, l+64, ... of that
+      // range, so each store instruction covers 64 consecutive pieces.
+      if (j > 0) stage_sync();  // the previous round's reads are done
+      if (c < a.n_chunks) {
+#pragma unroll
+        for (int q = 0; q < P; ++q) wave_stage[lane * P + q] = piece[q];
+      }
+      stage_sync();
+      const uint64_t wave_first_chunk = block_first + static_cast<uint64_t>(j) * QRS_BLOCK + (threadIdx.x & ~63);
+      u32x4 staged[P];
+#pragma unroll
+      for (int q = 0; q < P; ++q) staged[q] = wave_stage[q * 64 + lane];
+#pragma unroll
+      for (int q = 0; q < P; ++q) {
+        const int k = q * 64 + lane;  // piece k of the wave's range belongs to chunk k / P
+        if (wave_first_chunk + k / P < a.n_chunks) store_stream(out + wave_first_chunk * P + k, staged[q]);
+      }
+    }
+  }
+}
+
+template <int W, int XF, int SL, int OF>
+hipError_t launch_typed(const ReduceLaunch& l, hipStream_t stream) {
+  KernelArgs a;
+  for (int r = 0; r < kMaxWorld; ++r) {
+    a.x[r] = r < W ? static_cast<const u32x4*>(l.x[r]) : nullptr;
+    a.scales[r] = r < W ? l.scales[r] : nullptr;
+  }
+  a.out = l.out;
+  a.n_chunks = l.n_elems / kChunk;
+  const uint64_t per_block = static_cast<uint64_t>(QRS_BLOCK) * QRS_CHUNKS_PER_LANE;
+  const uint64_t blocks = (a.n_chunks + per_block - 1) / per_block;
+  if (blocks == 0 || blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF>), dim3(static_cast<uint32_t>(blocks)), dim3(QRS_BLOCK), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int W, int XF, int SL>
+hipError_t dispatch_out(const ReduceLaunch& l, hipStream_t s) {
+  return l.out_format == kOutF32 ? launch_typed<W, XF, SL, kOutF32>(l, s) : launch_typed<W, XF, SL, kOutBF16>(l, s);
+}
+
+template <int W>
+hipError_t dispatch_mode(const ReduceLaunch& l, hipStream_t s) {
+  if (l.scale_layout == kScaleE8M0Block32) {
+    switch (l.x_format) {
+      case kXE4M3FN: return dispatch_out<W, kXE4M3FN, kScaleE8M0Block32>(l, s);
+      case kXE5M2: return dispatch_out<W, kXE5M2, kScaleE8M0Block32>(l, s);
+      default: return hipErrorInvalidValue;  // INT8 has no MX mode
+    }
+  }
+  switch (l.x_format) {
+    case kXInt8: return dispatch_out<W, kXInt8, kScaleF32Group128>(l, s);
+    case kXE4M3FN: return dispatch_out<W, kXE4M3FN, kScaleF32Group128>(l, s);
+    case kXE5M2: return dispatch_out<W, kXE5M2, kScaleF32Group128>(l, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+__global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                          uint64_t n) {
+  const uint64_t i = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) store_stream(dst + i, load_stream(src + i));
+}
+
+}  // namespace
+
+hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream) {
+  switch (l.world_size) {
+    case 2: return dispatch_mode<2>(l, stream);
+    case 4: return dispatch_mode<4>(l, stream);
+    case 8: return dispatch_mode<8>(l, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_stream_copy(const void* src, void* dst, uint64_t bytes, hipStream_t stream) {
+  const uint64_t n = bytes / 16;
+  const uint64_t blocks = (n + 255) / 256;
+  if (blocks == 0 || blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
+  return hipGetLastError();
+}
+
+}  // namespace qrs

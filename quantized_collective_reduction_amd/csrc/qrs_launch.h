@@ -1,0 +1,40 @@
+// Internal interface between the C-ABI host library (qrs.cpp) and the gfx950
+// kernels (qrs_kernels.hip). Not installed; callers use include/qrs.h.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qrs {
+
+constexpr int kMaxWorld = 8;
+
+// Element and scale formats as the kernels see them.
+enum XFormat : int { kXInt8 = 0, kXE4M3FN = 1, kXE5M2 = 2 };
+enum ScaleLayout : int { kScaleF32Group128 = 0, kScaleE8M0Block32 = 1 };
+enum OutFormat : int { kOutF32 = 0, kOutBF16 = 1 };
+
+// One launch of the dequant + rank-ordered reduce over a flat [rows*H]
+// element range. Every slice is contiguous row-major, so element e of the
+// share lives at offset e in every x slice and in the output, and its scale
+// at offset e / G in every scale slice (G divides H).
+struct ReduceLaunch {
+  int world_size;          // 2, 4 or 8
+  XFormat x_format;
+  ScaleLayout scale_layout;
+  OutFormat out_format;
+  uint64_t n_elems;        // rows * H, a multiple of 128
+  const void* x[kMaxWorld];
+  const void* scales[kMaxWorld];
+  void* out;
+};
+
+hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream);
+
+// Plain 16-byte-per-lane device copy (bytes % 16 == 0, both pointers 16-byte
+// aligned): the reference stream for bandwidth and traffic-counter
+// calibration.
+hipError_t launch_stream_copy(const void* src, void* dst, uint64_t bytes, hipStream_t stream);
+
+}  // namespace qrs

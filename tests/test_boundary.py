@@ -1,0 +1,170 @@
+"""The C-ABI boundary on the host: the library loads, exports every function
+include/qrs.h declares, and rejects invalid problems before any GPU work.
+No compute call is made here (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_collective_reduction_amd as qrs
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "qrs.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return qrs.load_library()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qrs_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declarations_are_exported(lib):
+    declared = _declared_functions()
+    assert declared == sorted(qrs.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in qrs.Status:
+        assert lib.qrs_status_string(int(s)).decode() == f"QRS_{'OK' if s == 0 else 'ERR_' + s.name}"
+    assert lib.qrs_status_string(99).decode() == "QRS_ERR_UNKNOWN"
+
+
+VALID_MODES = [
+    ("int8", "f32_group128"),
+    ("e4m3fn", "f32_group128"),
+    ("e5m2", "f32_group128"),
+    ("e4m3fn", "e8m0_block32"),
+    ("e5m2", "e8m0_block32"),
+]
+
+
+@pytest.mark.parametrize("x,s", VALID_MODES)
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("w", [2, 4, 8])
+def test_valid_plans(lib, x, s, out, w):
+    p = qrs.plan(w, 16 * w, 1024, x, s, out)
+    assert p.rows == 16 and p.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("h", [1024, 1152, 4096, 5120, 7168, 8192])
+def test_accepted_h(lib, h):
+    assert qrs.plan(2, 2, h, "e4m3fn", "e8m0_block32", "bf16").rows == 1
+
+
+@pytest.mark.parametrize(
+    "args,status",
+    [
+        ((0, 16, 1024, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((1, 16, 1024, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((3, 18, 1024, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((5, 20, 1024, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((16, 32, 1024, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((2, 16, 1000, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((2, 16, 896, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((2, 16, 8320, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((2, 16, 1088, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((2, 0, 1024, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((2, -2, 1024, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((4, 18, 1024, "int8", "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((2, 16, 1024, "int8", "e8m0_block32", "f32"), qrs.Status.INVALID_ARG),
+        ((2, 16, 1024, "hifloat8", "f32_group128", "f32"), qrs.Status.UNSUPPORTED),
+        ((2, 16, 1024, 7, "f32_group128", "f32"), qrs.Status.INVALID_ARG),
+        ((2, 16, 1024, "int8", 5, "f32"), qrs.Status.INVALID_ARG),
+        ((2, 16, 1024, "int8", "f32_group128", 9), qrs.Status.INVALID_ARG),
+    ],
+)
+def test_rejected_plans(lib, args, status):
+    with pytest.raises(qrs.QrsError) as ei:
+        qrs.plan(*args)
+    assert ei.value.status == status
+    assert str(ei.value)
+
+
+def test_null_out_params(lib):
+    ws = ctypes.c_size_t()
+    h = ctypes.c_void_p(1234)
+    assert lib.qrs_plan(2, 16, 1024, 0, 0, 0, None, ctypes.byref(ws)) == qrs.Status.INVALID_ARG
+    assert lib.qrs_plan(2, 16, 1024, 0, 0, 0, ctypes.byref(h), None) == qrs.Status.INVALID_ARG
+    assert h.value is None  # cleared on error
+    assert b"non-null" in lib.qrs_last_error()
+
+
+def test_destroy_null_and_shape_of_null(lib):
+    assert lib.qrs_plan_destroy(None) == qrs.Status.OK
+    assert lib.qrs_plan_shape(None, None, None) == qrs.Status.INVALID_ARG
+
+
+# qrs_run checks its arguments on the host before it touches the GPU; these
+# calls return before any HIP call.
+
+
+def _run_raw(lib, p, xs, ss, out):
+    w = len(xs)
+    xa = (ctypes.c_void_p * w)(*xs)
+    sa = (ctypes.c_void_p * w)(*ss)
+    return lib.qrs_run(p.handle if p else None, xa, sa, out, None, 0, None)
+
+
+def test_run_rejects_bad_pointers_on_host(lib):
+    p = qrs.plan(2, 32, 1024, "e4m3fn", "f32_group128", "f32")
+    n = p.rows * p.h
+    A = 1 << 40  # fake, never dereferenced: every call below fails its host checks
+    good_x = [A, A + (1 << 30)]
+    good_s = [A + (2 << 30), A + (3 << 30)]
+    out = A + (4 << 30)
+    assert _run_raw(lib, None, good_x, good_s, out) == qrs.Status.INVALID_ARG
+    assert lib.qrs_run(p.handle, None, None, out, None, 0, None) == qrs.Status.INVALID_ARG
+    assert _run_raw(lib, p, good_x, good_s, 0) == qrs.Status.INVALID_ARG
+    assert _run_raw(lib, p, [A, 0], good_s, out) == qrs.Status.INVALID_ARG
+    assert _run_raw(lib, p, [A + 8, good_x[1]], good_s, out) == qrs.Status.INVALID_ARG  # x misaligned
+    assert _run_raw(lib, p, good_x, [good_s[0] + 2, good_s[1]], out) == qrs.Status.INVALID_ARG  # fp32 scale
+    assert _run_raw(lib, p, good_x, good_s, out + 4) == qrs.Status.INVALID_ARG  # out misaligned
+    # out overlapping an x slice or a scale slice
+    assert _run_raw(lib, p, good_x, good_s, good_x[1] + n - 16) == qrs.Status.INVALID_ARG
+    assert _run_raw(lib, p, good_x, good_s, good_s[0] - 16) == qrs.Status.INVALID_ARG
+    assert b"overlaps" in lib.qrs_last_error()
+
+
+def test_stream_copy_rejects_bad_arguments_on_host(lib):
+    A = 1 << 40
+    assert lib.qrs_stream_copy(None, A, 16, None) == qrs.Status.INVALID_ARG
+    assert lib.qrs_stream_copy(A, A + 4096, 0, None) == qrs.Status.INVALID_ARG
+    assert lib.qrs_stream_copy(A, A + 4096, 24, None) == qrs.Status.INVALID_ARG
+    assert lib.qrs_stream_copy(A + 8, A + 4096, 16, None) == qrs.Status.INVALID_ARG
+    assert lib.qrs_stream_copy(A, A + 16, 32, None) == qrs.Status.INVALID_ARG
+
+
+def test_binding_rejects_host_tensors_and_wrong_sizes(lib):
+    import torch
+
+    p = qrs.plan(2, 32, 1024, "e4m3fn", "f32_group128", "f32")
+    x = [torch.zeros(16, 1024, dtype=torch.uint8) for _ in range(2)]
+    s = [torch.zeros(16, 8, dtype=torch.float32) for _ in range(2)]
+    out = torch.zeros(16, 1024, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        qrs.run(p, x, s, out)  # CPU tensors: no CPU path
+    with pytest.raises(ValueError):
+        qrs.run(p, x[:1], s, out)
+    with pytest.raises(ValueError):
+        qrs.run(p, x, [torch.zeros(16, 4, dtype=torch.float32)] * 2, out)
+
+
+def test_prepared_launch_checks_arguments_on_host(lib):
+    import torch
+
+    p = qrs.plan(2, 32, 1024, "e4m3fn", "e8m0_block32", "bf16")
+    x = [torch.zeros(16, 1024, dtype=torch.uint8) for _ in range(2)]
+    s = [torch.zeros(16, 32, dtype=torch.uint8) for _ in range(2)]
+    out = torch.zeros(16, 1024, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        qrs.Launch(p, x, s, out)  # CPU tensors
+    with pytest.raises(ValueError):
+        qrs.Launch(p, x, s, torch.zeros(16, 1024, dtype=torch.float32))  # wrong output size

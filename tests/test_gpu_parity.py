@@ -1,0 +1,194 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+fp32 output must be bit-exact; bf16 output within 1 bf16 ulp (and the count
+of non-identical elements is reported). The five workloads run at their full
+sizes and are compared element by element, plus against the stored digests
+of the oracle's output; a sweep covers every mode, world size and several H
+at small, ragged row counts.
+"""
+
+import hashlib
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_util import assert_parity, empty_out, log, oracle_bits, out_bits, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "digests.json")
+
+MODES = [
+    ("int8", "f32_group128"),
+    ("e4m3fn", "f32_group128"),
+    ("e5m2", "f32_group128"),
+    ("e4m3fn", "e8m0_block32"),
+    ("e5m2", "e8m0_block32"),
+]
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
+def test_workload_full_size(gpu, name):
+    wl = workloads.CONFIGS[name]
+    log(f"[parity] {name}: W={wl.world_size} BS={wl.bs} H={wl.h} {wl.x_format}/{wl.scale_layout}->{wl.out_dtype}")
+    xs, ss = workloads.generate(wl)
+    got = run_gpu(wl.world_size, wl.rows, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype, xs, ss)
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype), wl.out_dtype)
+    n_diff = assert_parity(got, want, wl.out_dtype, name)
+    log(f"[parity] {name}: {got.size} elements, {n_diff} not bit-identical")
+    with open(GOLDEN) as f:
+        digest = json.load(f)["configs"][name]["output_sha256"]
+    if n_diff == 0:
+        assert hashlib.sha256(got.tobytes()).hexdigest() == digest
+
+
+@pytest.mark.parametrize("x_format,scale_layout", MODES)
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("w", [2, 4, 8])
+@pytest.mark.parametrize("h", [1024, 1152, 5120, 8192])
+def test_sweep_small_ragged(gpu, x_format, scale_layout, out_dtype, w, h):
+    # rows chosen so the element count is not a multiple of a block's span.
+    rows = 3 if h == 8192 else 5
+    wl = workloads.Workload(
+        "sweep", w, rows * w, h, x_format, scale_layout, out_dtype,
+        x_dist="int_uniform" if x_format == "int8" else "normal",
+        x_param=127 if x_format == "int8" else (64 if x_format == "e4m3fn" else 2048),
+        scale_lo=-20 if scale_layout == "f32_group128" else 100,
+        scale_hi=4 if scale_layout == "f32_group128" else 150,
+        seed=1000 + w * 7 + h,
+    )
+    xs, ss = workloads.generate(wl)
+    got = run_gpu(w, rows, h, x_format, scale_layout, out_dtype, xs, ss)
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, x_format, scale_layout, out_dtype), out_dtype)
+    assert_parity(got, want, out_dtype, f"W={w} H={h} {x_format}/{scale_layout}->{out_dtype}")
+
+
+@pytest.mark.parametrize("rows", [1, 2, 7, 63, 64, 65, 257])
+def test_row_counts_around_block_edges(gpu, rows):
+    wl = workloads.CONFIGS["C4"].with_(bs=8 * rows, h=1152)
+    xs, ss = workloads.generate(wl)
+    got = run_gpu(8, rows, 1152, wl.x_format, wl.scale_layout, "f32", xs, ss)
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, "f32"), "f32")
+    assert_parity(got, want, "f32", f"rows={rows}")
+
+
+def test_non_finite_and_extreme_codes(gpu):
+    """Every code including NaN / inf, every E8M0 code including 0 and 255,
+    fp32 scales with zeros, negatives, subnormals and huge values."""
+    rng = np.random.default_rng(99)
+    for x_format, scale_layout in MODES:
+        for out_dtype in ("f32", "bf16"):
+            w, rows, h = 4, 16, 1024
+            g = 128 if scale_layout == "f32_group128" else 32
+            xs = [rng.integers(0, 256, size=(rows, h), dtype=np.uint8) for _ in range(w)]
+            if scale_layout == "f32_group128":
+                bits = rng.integers(0, 2**32, size=(w, rows, h // g), dtype=np.uint64).astype(np.uint32)
+                ss = [b.view(np.float32) for b in bits]
+            else:
+                ss = [rng.integers(0, 256, size=(rows, h // g), dtype=np.uint8) for _ in range(w)]
+            got = run_gpu(w, rows, h, x_format, scale_layout, out_dtype, xs, ss)
+            want = oracle_bits(oracle.reduce_scatter_share(xs, ss, x_format, scale_layout, out_dtype), out_dtype)
+            assert_parity(got, want, out_dtype, f"{x_format}/{scale_layout}->{out_dtype}")
+
+
+def test_slices_in_separate_allocations_and_one_buffer(gpu):
+    """The pointer-array form: separate tensors per rank, or views into one
+    [W, rows, H] buffer, give the same bits."""
+    import quantized_collective_reduction_amd as qrs
+
+    wl = workloads.CONFIGS["C3"].with_(bs=8 * 40, h=2048)
+    xs, ss = workloads.generate(wl)
+    p = qrs.plan(8, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    dx, ds = to_device(xs, ss)
+    o1 = empty_out(wl.rows, wl.h, wl.out_dtype)
+    qrs.run(p, dx, ds, o1)
+    bx = torch.stack(dx)
+    bs_ = torch.stack(ds)
+    o2 = empty_out(wl.rows, wl.h, wl.out_dtype)
+    qrs.run(p, [bx[r] for r in range(8)], [bs_[r] for r in range(8)], o2)
+    # Fresh copies at other addresses: only the pointer array fixes which slice is which rank.
+    o3 = empty_out(wl.rows, wl.h, wl.out_dtype)
+    qrs.run(p, [t.clone() for t in dx], [t.clone() for t in ds], o3)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_bits(o1), out_bits(o2))
+    assert np.array_equal(out_bits(o1), out_bits(o3))
+
+
+def test_runs_on_the_given_stream(gpu):
+    """The kernel is ordered after earlier work on a non-default stream."""
+    import quantized_collective_reduction_amd as qrs
+
+    wl = workloads.CONFIGS["C2"].with_(bs=4 * 256)
+    xs, ss = workloads.generate(wl)
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype), wl.out_dtype)
+    p = qrs.plan(4, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    s = torch.cuda.Stream()
+    dx = [torch.zeros(wl.rows, wl.h, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    ds = [torch.zeros(wl.rows, wl.h // 128, dtype=torch.float32, device="cuda") for _ in range(4)]
+    hx = [torch.from_numpy(x).pin_memory() for x in xs]
+    hs = [torch.from_numpy(v).pin_memory() for v in ss]
+    out = empty_out(wl.rows, wl.h, wl.out_dtype)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        # Big slow-ish work first on the same stream, then the copies, then the run.
+        junk = torch.empty(64 << 20, dtype=torch.float32, device="cuda")
+        for _ in range(4):
+            junk.mul_(1.0001)
+        for r in range(4):
+            dx[r].copy_(hx[r], non_blocking=True)
+            ds[r].copy_(hs[r], non_blocking=True)
+        qrs.run(p, dx, ds, out)  # current stream is s
+    s.synchronize()
+    assert_parity(out_bits(out), want, wl.out_dtype, "stream order")
+
+
+def test_misaligned_device_pointers_rejected(gpu):
+    import quantized_collective_reduction_amd as qrs
+
+    p = qrs.plan(2, 32, 1024, "e4m3fn", "e8m0_block32", "f32")
+    x = torch.zeros(2, 16 * 1024 + 16, dtype=torch.uint8, device="cuda")
+    s = torch.zeros(2, 16 * 32 + 16, dtype=torch.uint8, device="cuda")  # room for offset views
+    out = torch.zeros(16 * 1024 + 4, dtype=torch.float32, device="cuda")
+    with pytest.raises(qrs.QrsError) as ei:
+        qrs.run(p, [x[0, 8:].data_ptr(), x[1, :16384].data_ptr()], [s[0, :512], s[1, :512]], out[:16384])
+    assert ei.value.status == qrs.Status.INVALID_ARG
+    with pytest.raises(qrs.QrsError):
+        qrs.run(p, [x[0, :16384], x[1, :16384]], [s[0, :512], s[1, :512]], out[1:16385].data_ptr())
+    # E8M0 scales have no alignment requirement.
+    qrs.run(p, [x[0, :16384], x[1, :16384]], [s[0, 1:].data_ptr(), s[1, 3:].data_ptr()], out[:16384])
+    torch.cuda.synchronize()
+
+
+def test_stream_copy(gpu):
+    import quantized_collective_reduction_amd as qrs
+
+    src = torch.randint(0, 255, (3 << 20,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    qrs.stream_copy(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
+
+
+def test_prepared_launch_matches_run(gpu):
+    """qrs.Launch (arguments marshalled once) gives the same bits as qrs.run."""
+    import quantized_collective_reduction_amd as qrs
+
+    wl = workloads.CONFIGS["C5"].with_(bs=8 * 33)
+    xs, ss = workloads.generate(wl)
+    p = qrs.plan(8, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    dx, ds = to_device(xs, ss)
+    o1 = empty_out(wl.rows, wl.h, wl.out_dtype)
+    o2 = empty_out(wl.rows, wl.h, wl.out_dtype)
+    qrs.run(p, dx, ds, o1)
+    launch = qrs.Launch(p, dx, ds, o2)
+    launch()
+    launch()
+    torch.cuda.synchronize()
+    assert np.array_equal(out_bits(o1), out_bits(o2))
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype), wl.out_dtype)
+    assert_parity(out_bits(o2), want, wl.out_dtype, "Launch")

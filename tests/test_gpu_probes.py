@@ -1,0 +1,77 @@
+"""GPU probes of the conversions and the fold, through the real kernels.
+
+* Every x code of every format, alone in rank 0 with a unit scale: the
+  output must be the code's exact value (catches a wrong fp8 flavour, NaN,
+  infinity or subnormal handling in the hardware conversions).
+* Every E8M0 code as the scale of x = 1: the output is the scale's value
+  (catches the 2^-127 subnormal and the NaN code).
+* The hand-derived worked examples (tests/golden/worked_examples.json):
+  the kernel must reproduce the expected bits, which fix the fold order, the
+  fold's start, the separate rounding of product and sum, and bf16 ties.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import assert_parity, oracle_bits, run_gpu
+from test_oracle_closed_forms import build_example, load_worked_examples
+
+pytestmark = pytest.mark.gpu
+
+ONE_CODE = {"int8": 0x01, "e4m3fn": 0x38, "e5m2": 0x3C}
+
+
+@pytest.mark.parametrize(
+    "x_format,scale_layout",
+    [("int8", "f32_group128"), ("e4m3fn", "f32_group128"), ("e5m2", "f32_group128"),
+     ("e4m3fn", "e8m0_block32"), ("e5m2", "e8m0_block32")],
+)
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_every_x_code_decodes_exactly(gpu, x_format, scale_layout, out_dtype):
+    rows, h = 2, 1024
+    codes = np.tile(np.arange(256, dtype=np.uint8), rows * h // 256).reshape(rows, h)
+    zero = np.zeros_like(codes)
+    g = 128 if scale_layout == "f32_group128" else 32
+    if scale_layout == "f32_group128":
+        unit = np.ones((rows, h // g), dtype=np.float32)
+    else:
+        unit = np.full((rows, h // g), 127, dtype=np.uint8)
+    got = run_gpu(2, rows, h, x_format, scale_layout, out_dtype, [codes, zero], [unit, unit])
+    want = oracle_bits(oracle.reduce_scatter_share([codes, zero], [unit, unit], x_format, scale_layout, out_dtype),
+                       out_dtype)
+    assert_parity(got, want, out_dtype, f"{x_format} codes")
+    if out_dtype == "f32":
+        table = oracle.decode_table(x_format)
+        vals = got.view(np.float32).reshape(-1)[:256]
+        nan = np.isnan(table)
+        assert np.array_equal(np.isnan(vals), nan)
+        # x + 0: exact except that -0 + +0 = +0.
+        expect = np.where(table == 0, np.float32(0.0), table)
+        assert np.array_equal(vals[~nan].view(np.uint32), expect[~nan].view(np.uint32))
+
+
+@pytest.mark.parametrize("x_format", ["e4m3fn", "e5m2"])
+def test_every_e8m0_code(gpu, x_format):
+    rows, h = 1, 8192  # 256 scale blocks in one row
+    one = np.full((rows, h), ONE_CODE[x_format], dtype=np.uint8)
+    zero = np.zeros_like(one)
+    codes = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    unit = np.full((1, 256), 127, dtype=np.uint8)
+    got = run_gpu(2, rows, h, x_format, "e8m0_block32", "f32", [one, zero], [codes, unit])
+    want = oracle_bits(oracle.reduce_scatter_share([one, zero], [codes, unit], x_format, "e8m0_block32", "f32"), "f32")
+    assert_parity(got, want, "f32", "e8m0 codes")
+    vals = got.view(np.float32).reshape(256, 32)[:, 0]
+    st = oracle.scale_decode_table()
+    assert np.isnan(vals[255])
+    assert np.array_equal(vals[:255].view(np.uint32), st[:255].view(np.uint32))
+    assert vals[0].view(np.uint32) == 0x00400000  # 2^-127 kept as a subnormal
+
+
+@pytest.mark.parametrize("ex", load_worked_examples(), ids=lambda e: e["name"])
+def test_worked_example_on_gpu(gpu, ex):
+    rows, h = 2, 1024
+    xs, ss = build_example(ex, rows=rows, h=h)
+    got = run_gpu(len(xs), rows, h, ex["x_format"], ex["scale_layout"], ex["out_dtype"], xs, ss)
+    want = int(ex["expected_bits"], 16)
+    assert np.all(got == want), (ex["name"], hex(int(got.ravel()[0])), hex(want))
