@@ -53,10 +53,11 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def read_traffic(workload_name):
-    """HBM bytes per launch from profiles/traffic_<workload>.txt, if that
-    summary was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_reduce_{workload_name}.txt")
+def read_traffic(workload_name, op):
+    """HBM bytes per launch from profiles/traffic_<op>_<workload>.txt, if
+    that summary was taken on the current kernel source; else None."""
+    stem = "reduce" if op == "share" else op
+    path = os.path.join(ROOT, "profiles", f"traffic_{stem}_{workload_name}.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -97,12 +98,63 @@ def cpu_baseline(wl, xs, ss, min_seconds=10.0, min_reps=3):
     }
 
 
+def setup_share(wl, dev, qrs, workloads, torch):
+    """This GPU's share (qrs_run): W slices [rows, H] -> [rows, H]."""
+    alg_bytes = wl.algorithmic_bytes()
+    t0 = time.perf_counter()
+    xs, ss = workloads.generate(wl)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    n_sets = max(2, -(-4 * MALL_BYTES // alg_bytes))
+    out_dt = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
+    dx0 = [torch.from_numpy(x).to(dev) for x in xs]
+    ds0 = [torch.from_numpy(s).to(dev) for s in ss]
+    p = qrs.plan(wl.world_size, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    stream = torch.cuda.current_stream(dev)
+    launches, outs = [], []
+    for k in range(n_sets):
+        dx = dx0 if k == 0 else [t.clone() for t in dx0]
+        ds = ds0 if k == 0 else [t.clone() for t in ds0]
+        out = torch.empty((wl.rows, wl.h), dtype=out_dt, device=dev)
+        launches.append(qrs.Launch(p, dx, ds, out, stream=stream))
+        outs.append([out])
+    return alg_bytes, launches, outs, (xs, ss)
+
+
+def setup_all_shares(wl, dev, qrs, workloads, torch):
+    """The group's whole reduce-scatter on this GPU (qrs_run_all_shares):
+    W inputs [BS, H] -> W shares [BS/W, H], the all-to-all by addressing."""
+    alg_bytes = wl.world_size * wl.algorithmic_bytes()
+    t0 = time.perf_counter()
+    xs, ss = workloads.generate_full(wl)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    n_sets = max(2, -(-4 * MALL_BYTES // alg_bytes))
+    out_dt = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
+    dx0 = [torch.from_numpy(x).to(dev) for x in xs]
+    ds0 = [torch.from_numpy(s).to(dev) for s in ss]
+    p = qrs.plan(wl.world_size, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    stream = torch.cuda.current_stream(dev)
+    launches, outs = [], []
+    for k in range(n_sets):
+        dx = dx0 if k == 0 else [t.clone() for t in dx0]
+        ds = ds0 if k == 0 else [t.clone() for t in ds0]
+        o = [torch.empty((wl.rows, wl.h), dtype=out_dt, device=dev) for _ in range(wl.world_size)]
+        launches.append(qrs.AllSharesLaunch(p, dx, ds, o, stream=stream))
+        outs.append(o)
+    return alg_bytes, launches, outs, None
+
+
+OPS = {"share": setup_share, "all_shares": setup_all_shares}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="C4", help="C1..C5 (default C4: W=8, H=8192, the metric's workload)")
+    ap.add_argument("--op", default="share", choices=sorted(OPS),
+                    help="share: this GPU's share (the hot path, default); all_shares: every rank's share "
+                         "from the inputs before the all-to-all, in one launch")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (cpu_baseline = null)")
     args = ap.parse_args()
 
@@ -125,40 +177,24 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = workloads.CONFIGS[args.workload]
-    alg_bytes = wl.algorithmic_bytes()
-    log(f"[bench] {wl.name}: W={wl.world_size} BS={wl.bs} H={wl.h} rows={wl.rows} "
-        f"{wl.x_format}/{wl.scale_layout}->{wl.out_dtype}, {alg_bytes} algorithmic bytes per step")
-
-    t0 = time.perf_counter()
-    xs, ss = workloads.generate(wl)
-    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
-
-    # Rotating sets: enough that consecutive steps touch over 4x the Infinity Cache.
-    n_sets = max(2, -(-4 * MALL_BYTES // alg_bytes))
-    out_dt = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
-    dx0 = [torch.from_numpy(x).to(dev) for x in xs]
-    ds0 = [torch.from_numpy(s).to(dev) for s in ss]
-    sets = []
-    for k in range(n_sets):
-        dx = dx0 if k == 0 else [t.clone() for t in dx0]
-        ds = ds0 if k == 0 else [t.clone() for t in ds0]
-        out = torch.empty((wl.rows, wl.h), dtype=out_dt, device=dev)
-        sets.append((dx, ds, out))
-    p = qrs.plan(wl.world_size, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    log(f"[bench] {args.op} on {wl.name}: W={wl.world_size} BS={wl.bs} H={wl.h} rows={wl.rows} "
+        f"{wl.x_format}/{wl.scale_layout}->{wl.out_dtype}")
+    alg_bytes, launches, outs, host_inputs = OPS[args.op](wl, dev, qrs, workloads, torch)
+    n_sets = len(launches)
     stream = torch.cuda.current_stream(dev)
-    launches = [qrs.Launch(p, dx, ds, out, stream=stream) for dx, ds, out in sets]
     torch.cuda.synchronize()
-    log(f"[bench] {n_sets} rotating input/output sets on {torch.cuda.get_device_name(dev)}")
+    log(f"[bench] {alg_bytes} algorithmic bytes per step; {n_sets} rotating input/output sets on "
+        f"{torch.cuda.get_device_name(dev)}")
 
     for i in range(args.warmup):
         launches[i % n_sets]()
     torch.cuda.synchronize()
     # All sets hold identical inputs, so every set must produce the same bits.
     if args.warmup >= n_sets:
-        ref = sets[0][2].view(torch.uint8)
-        for _, _, out in sets[1:]:
-            if not torch.equal(out.view(torch.uint8), ref):
-                sys.exit("rotating sets disagree: the kernel is not deterministic")
+        for o in outs[1:]:
+            for a, b in zip(o, outs[0]):
+                if not torch.equal(a.view(torch.uint8), b.view(torch.uint8)):
+                    sys.exit("rotating sets disagree: the kernel is not deterministic")
 
     # Timed region: K back-to-back launches, HIP events on the launch stream
     # at both ends, wall clock around it.
@@ -201,7 +237,7 @@ def main():
     achieved = alg_bytes / avg_launch_s / 1e9
     value = alg_bytes * args.steps / wall / 1e9
     result = {
-        "metric": METRIC,
+        "metric": METRIC if args.op == "share" else METRIC + " (all W shares in one launch)",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -215,7 +251,9 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: W={wl.world_size} BS={wl.bs} H={wl.h} x={wl.x_format} "
-                        f"scales={wl.scale_layout} out={wl.out_dtype}",
+                        f"scales={wl.scale_layout} out={wl.out_dtype}"
+                        + ("" if args.op == "share" else ", all W shares from the pre-all-to-all inputs"),
+            "op": args.op,
             "world_size": wl.world_size,
             "bs": wl.bs,
             "rows": wl.rows,
@@ -230,15 +268,15 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": read_traffic(wl.name),
+            "traffic": read_traffic(wl.name, args.op),
             "kernel_us_avg": round(avg_launch_s * 1e6, 3),
         },
         "copy_calibration": {"bytes_moved": 2 * copy_bytes, "GBps": round(copy_gbps, 1)},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and host_inputs is not None:
         log("[bench] timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(wl, xs, ss)
+        result["cpu_baseline"] = cpu_baseline(wl, *host_inputs)
         log(f"[bench] cpu baseline: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
 

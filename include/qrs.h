@@ -127,6 +127,34 @@ qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, 
 qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* const* scale_slices, void* out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The whole reduce-scatter of a W-rank group computed on this GPU: every
+ * rank's share, from the ranks' inputs as they are BEFORE the all-to-all.
+ * Page "aclnnQuantReduceScatter", Function description: the data and scales
+ * are all-to-all'ed, then reduced. The all-to-all splits each rank's [BS, H]
+ * rows into W row blocks of rows = BS/W and delivers block j of every rank
+ * to rank j (in rank order); here that index map is applied by addressing,
+ * with no copy, so share j is
+ *
+ *     out_shares[j] = Reduce_r( scales_r[block j] * x_r[block j] )
+ *
+ * with the same arithmetic as qrs_run. One launch covers all W shares.
+ *
+ *   x_full        HOST array of W DEVICE pointers; x_full[r] is rank r's
+ *                 uint8 codes [BS, H], contiguous, 16-byte aligned.
+ *   scale_full    HOST array of W DEVICE pointers to rank r's scales for all
+ *                 BS rows in the plan's layout ([BS, H/128] fp32, 4-byte
+ *                 aligned, or [BS, H/32] E8M0).
+ *   out_shares    HOST array of W DEVICE pointers; out_shares[j] is share
+ *                 j's [BS/W, H] output, 16-byte aligned, overlapping neither
+ *                 an input nor another share.
+ *   workspace, workspace_bytes, stream: as for qrs_run.
+ *
+ * Errors as for qrs_run.
+ */
+qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const void* const* scale_full,
+                              void* const* out_shares, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Free a plan. NULL is accepted. Plans in use by queued runs may be freed:
  * qrs_run copies what the kernel needs into its launch arguments. */
 qrs_status qrs_plan_destroy(qrs_plan_t plan);

@@ -18,6 +18,9 @@ Modules:
 * ``reduce`` -- the plain numpy definition: decode, multiply by the group or
   block scale with one fp32 rounding, left fold over ranks 0..W-1 in fp32,
   optional round-to-nearest-even to bf16 done in integer arithmetic.
+* ``reduce.all_to_all`` / ``reduce.all_shares`` -- the all-to-all index map
+  (rank r's row block j goes to rank j, received in rank order) followed by
+  the reduce on every rank: the whole group's reduce-scatter on one host.
 * ``exact`` -- brute force with ``fractions.Fraction``: exact products and
   sums, each rounded to binary32 by a rounding routine written from the
   IEEE 754 definition. Used to pin ``reduce`` on tiny inputs.
@@ -40,6 +43,8 @@ from .decode import (
     scale_decode_table,
 )
 from .reduce import (
+    all_shares,
+    all_to_all,
     dequantize_rank,
     reduce_scatter_share,
     fp32_to_bf16_bits,
@@ -53,6 +58,8 @@ __all__ = [
     "GROUP_SIZE",
     "decode_table",
     "scale_decode_table",
+    "all_shares",
+    "all_to_all",
     "dequantize_rank",
     "reduce_scatter_share",
     "fp32_to_bf16_bits",

@@ -121,3 +121,36 @@ def reduce_scatter_share(x_slices, scale_slices, x_format, scale_layout, out_dty
     if out_dtype == "f32":
         return acc
     return fp32_to_bf16_bits(acc)
+
+
+def all_to_all(x_full, scale_full):
+    """The all-to-all in front of the reduce (page "aclnnQuantReduceScatter",
+    Function description: both the data and the scales are all-to-all'ed).
+
+    ``x_full[r]`` is rank r's ``[BS, H]`` codes and ``scale_full[r]`` its
+    scales for all BS rows. Each rank splits its rows into W equal row blocks
+    and sends block j to rank j; rank j receives the blocks in rank order.
+    Returns, for each rank j, the list of received (x, scales) slices.
+    """
+    w = len(x_full)
+    if w == 0 or len(scale_full) != w:
+        raise ValueError("need W >= 1 inputs and as many scale tensors")
+    bs = x_full[0].shape[0]
+    if bs % w:
+        raise ValueError(f"BS={bs} is not a multiple of W={w}")
+    rows = bs // w
+    received = []
+    for j in range(w):
+        xs = [x_full[r][j * rows:(j + 1) * rows] for r in range(w)]
+        ss = [scale_full[r][j * rows:(j + 1) * rows] for r in range(w)]
+        received.append((xs, ss))
+    return received
+
+
+def all_shares(x_full, scale_full, x_format, scale_layout, out_dtype):
+    """Every rank's share of the quantized reduce-scatter: the all-to-all,
+    then on each rank the reduce of ``reduce_scatter_share``."""
+    return [
+        reduce_scatter_share(xs, ss, x_format, scale_layout, out_dtype)
+        for xs, ss in all_to_all(x_full, scale_full)
+    ]

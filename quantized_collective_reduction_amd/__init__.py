@@ -30,7 +30,9 @@ __all__ = [
     "load_library",
     "plan",
     "run",
+    "run_all_shares",
     "Launch",
+    "AllSharesLaunch",
     "stream_copy",
     "EXPORTED_SYMBOLS",
 ]
@@ -68,6 +70,7 @@ _OUT_NAMES = {"f32": OutDtype.F32, "bf16": OutDtype.BF16}
 EXPORTED_SYMBOLS = (
     "qrs_plan",
     "qrs_run",
+    "qrs_run_all_shares",
     "qrs_plan_destroy",
     "qrs_plan_shape",
     "qrs_status_string",
@@ -101,6 +104,8 @@ def load_library(path: str = LIB_PATH):
     lib.qrs_plan.restype = c_int
     lib.qrs_run.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, c_sz, vp]
     lib.qrs_run.restype = c_int
+    lib.qrs_run_all_shares.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), vp, c_sz, vp]
+    lib.qrs_run_all_shares.restype = c_int
     lib.qrs_plan_destroy.argtypes = [vp]
     lib.qrs_plan_destroy.restype = c_int
     lib.qrs_plan_shape.argtypes = [vp, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]
@@ -211,6 +216,28 @@ def run(p: Plan, x_slices, scale_slices, out, stream=None):
     _check(lib.qrs_run(p.handle, xs, ss, _ptr(out), None, 0, _stream_handle(stream)))
 
 
+def run_all_shares(p: Plan, x_full, scale_full, out_shares, stream=None):
+    """Every rank's share from the ranks' inputs before the all-to-all.
+
+    ``x_full[r]``: rank r's ``[BS, H]`` codes; ``scale_full[r]``: its scales
+    for all BS rows; ``out_shares[j]``: share j's ``[BS/W, H]`` output.
+    """
+    lib = load_library()
+    w = p.world_size
+    if len(x_full) != w or len(scale_full) != w or len(out_shares) != w:
+        raise ValueError(f"need {w} inputs, {w} scale tensors and {w} outputs")
+    n = p.rows * p.h
+    scale_bytes = n // 128 * 4 if p.scale_layout == ScaleLayout.F32_GROUP128 else n // 32
+    for r in range(w):
+        _check_tensor(x_full[r], n * w, f"x of rank {r}")
+        _check_tensor(scale_full[r], scale_bytes * w, f"scales of rank {r}")
+        _check_tensor(out_shares[r], n * (4 if p.out_dtype == OutDtype.F32 else 2), f"output of share {r}")
+    xs = (ctypes.c_void_p * w)(*[_ptr(t) for t in x_full])
+    ss = (ctypes.c_void_p * w)(*[_ptr(t) for t in scale_full])
+    os_ = (ctypes.c_void_p * w)(*[_ptr(t) for t in out_shares])
+    _check(lib.qrs_run_all_shares(p.handle, xs, ss, os_, None, 0, _stream_handle(stream)))
+
+
 class Launch:
     """Arguments for ``run`` marshalled once, for repeated launches of one
     plan on fixed buffers (each call is a single C call: no per-call Python
@@ -238,6 +265,35 @@ class Launch:
 
     def __call__(self):
         status = self._fn(self._handle, self._xs, self._ss, self._out, None, 0, self._stream)
+        if status:
+            _check(status)
+
+
+class AllSharesLaunch:
+    """``run_all_shares`` with its arguments marshalled once."""
+
+    def __init__(self, p: Plan, x_full, scale_full, out_shares, stream=None):
+        lib = load_library()
+        w = p.world_size
+        if len(x_full) != w or len(scale_full) != w or len(out_shares) != w:
+            raise ValueError(f"need {w} inputs, {w} scale tensors and {w} outputs")
+        n = p.rows * p.h
+        scale_bytes = n // 128 * 4 if p.scale_layout == ScaleLayout.F32_GROUP128 else n // 32
+        for r in range(w):
+            _check_tensor(x_full[r], n * w, f"x of rank {r}")
+            _check_tensor(scale_full[r], scale_bytes * w, f"scales of rank {r}")
+            _check_tensor(out_shares[r], n * (4 if p.out_dtype == OutDtype.F32 else 2), f"output of share {r}")
+        self._plan = p
+        self._keep = (list(x_full), list(scale_full), list(out_shares))
+        self._xs = (ctypes.c_void_p * w)(*[_ptr(t) for t in x_full])
+        self._ss = (ctypes.c_void_p * w)(*[_ptr(t) for t in scale_full])
+        self._os = (ctypes.c_void_p * w)(*[_ptr(t) for t in out_shares])
+        self._stream = ctypes.c_void_p(_stream_handle(stream))
+        self._fn = lib.qrs_run_all_shares
+        self._handle = p.handle
+
+    def __call__(self):
+        status = self._fn(self._handle, self._xs, self._ss, self._os, None, 0, self._stream)
         if status:
             _check(status)
 

@@ -139,7 +139,8 @@ qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* con
   l.scale_layout = plan->scale_layout;
   l.out_format = plan->out_format;
   l.n_elems = n;
-  l.out = out;
+  l.n_shares = 1;
+  l.out[0] = out;
   for (int r = 0; r < W; ++r) {
     if (!x_slices[r] || !scale_slices[r]) return fail(QRS_ERR_INVALID_ARG, "null slice pointer for rank %d", r);
     if (!aligned(x_slices[r], 16)) return fail(QRS_ERR_INVALID_ARG, "x slice of rank %d is not 16-byte aligned", r);
@@ -149,6 +150,54 @@ qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* con
       return fail(QRS_ERR_INVALID_ARG, "out overlaps an input slice of rank %d", r);
     l.x[r] = x_slices[r];
     l.scales[r] = scale_slices[r];
+  }
+  const hipError_t e = qrs::launch_reduce(l, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const void* const* scale_full,
+                              void* const* out_shares, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!plan) return fail(QRS_ERR_INVALID_ARG, "null plan");
+  if (!x_full || !scale_full || !out_shares) return fail(QRS_ERR_INVALID_ARG, "null pointer array");
+  const int W = plan->world_size;
+  const uint64_t n = static_cast<uint64_t>(plan->rows) * static_cast<uint64_t>(plan->h);  // per share
+  const bool f32_scales = plan->scale_layout == qrs::kScaleF32Group128;
+  const uint64_t share_scale_bytes = f32_scales ? n / 128 * 4 : n / 32;
+  const uint64_t out_bytes = n * (plan->out_format == qrs::kOutF32 ? 4 : 2);
+  const uint64_t full_x_bytes = n * W, full_scale_bytes = share_scale_bytes * W;
+
+  qrs::ReduceLaunch l;
+  std::memset(&l, 0, sizeof(l));
+  l.world_size = W;
+  l.x_format = plan->x_format;
+  l.scale_layout = plan->scale_layout;
+  l.out_format = plan->out_format;
+  l.n_elems = n;
+  l.n_shares = W;
+  l.x_share_stride = n;  // row block j of rank r starts j * rows * H bytes into x_full[r]
+  l.scale_share_stride = share_scale_bytes;
+  for (int j = 0; j < W; ++j) {
+    if (!out_shares[j]) return fail(QRS_ERR_INVALID_ARG, "null output for share %d", j);
+    if (!aligned(out_shares[j], 16)) return fail(QRS_ERR_INVALID_ARG, "output of share %d is not 16-byte aligned", j);
+    for (int k = 0; k < j; ++k)
+      if (overlaps(out_shares[j], out_bytes, out_shares[k], out_bytes))
+        return fail(QRS_ERR_INVALID_ARG, "outputs of shares %d and %d overlap", k, j);
+    l.out[j] = out_shares[j];
+  }
+  for (int r = 0; r < W; ++r) {
+    if (!x_full[r] || !scale_full[r]) return fail(QRS_ERR_INVALID_ARG, "null input pointer for rank %d", r);
+    if (!aligned(x_full[r], 16)) return fail(QRS_ERR_INVALID_ARG, "x of rank %d is not 16-byte aligned", r);
+    if (f32_scales && !aligned(scale_full[r], 4))
+      return fail(QRS_ERR_INVALID_ARG, "fp32 scales of rank %d are not 4-byte aligned", r);
+    for (int j = 0; j < W; ++j)
+      if (overlaps(out_shares[j], out_bytes, x_full[r], full_x_bytes) ||
+          overlaps(out_shares[j], out_bytes, scale_full[r], full_scale_bytes))
+        return fail(QRS_ERR_INVALID_ARG, "output of share %d overlaps an input of rank %d", j, r);
+    l.x[r] = x_full[r];
+    l.scales[r] = scale_full[r];
   }
   const hipError_t e = qrs::launch_reduce(l, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -56,6 +56,13 @@
 #ifndef QRS_STAGE_STORES
 #define QRS_STAGE_STORES 1
 #endif
+// Block-to-XCD placement: the hardware hands consecutive block ids to the
+// 8 XCDs in turn. With 1, block id b is renumbered so that XCD b % 8 walks
+// one contiguous eighth of the element range (each XCD's L2 and TLB then
+// see 1/8 of the pages). Needs a block count divisible by 8 to apply.
+#ifndef QRS_XCD_REMAP
+#define QRS_XCD_REMAP 0
+#endif
 // 1: block barrier around the LDS exchange; 0: wave-local ordering only.
 #ifndef QRS_STAGE_BLOCK_SYNC
 #define QRS_STAGE_BLOCK_SYNC 0
@@ -136,8 +143,10 @@ __device__ __forceinline__ float load_scale(const void* base, uint64_t chunk) {
 struct KernelArgs {
   const u32x4* x[kMaxWorld];
   const void* scales[kMaxWorld];
-  void* out;
-  uint64_t n_chunks;
+  void* out[kMaxWorld];  // one per share (blockIdx.y)
+  uint64_t n_chunks;     // chunks per share
+  uint64_t x_share_stride;      // in 16-byte units
+  uint64_t scale_share_stride;  // in bytes
 };
 
 // Orders a wave's LDS writes before its following LDS reads of other lanes'
@@ -222,8 +231,17 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
   constexpr int P = OutPieces<OF>::kCount;
   // Chunk j of this lane is base + j*QRS_BLOCK: every load instruction of a
   // wave covers one contiguous range.
-  const uint64_t block_first = static_cast<uint64_t>(blockIdx.x) * (QRS_BLOCK * CH);
+  uint32_t block_id = blockIdx.x;
+#if QRS_XCD_REMAP
+  if ((gridDim.x & 7u) == 0) block_id = (block_id & 7u) * (gridDim.x >> 3) + (block_id >> 3);
+#endif
+  const uint64_t block_first = static_cast<uint64_t>(block_id) * (QRS_BLOCK * CH);
   const uint64_t base = block_first + threadIdx.x;
+  // Share handled by this block (one share unless the all-to-all is
+  // emulated on this GPU): uniform offsets into every rank's input.
+  const uint32_t share = blockIdx.y;
+  const uint64_t x_off = share * a.x_share_stride;
+  const uint64_t s_off = share * a.scale_share_stride;
 
   u32x4 xv[CH][W];
   float sv[CH][W];
@@ -232,13 +250,13 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
     const uint64_t c = base + static_cast<uint64_t>(j) * QRS_BLOCK;
     if (c < a.n_chunks) {
 #pragma unroll
-      for (int r = 0; r < W; ++r) xv[j][r] = load_stream(a.x[r] + c);
+      for (int r = 0; r < W; ++r) xv[j][r] = load_stream(a.x[r] + x_off + c);
 #pragma unroll
-      for (int r = 0; r < W; ++r) sv[j][r] = load_scale<SL>(a.scales[r], c);
+      for (int r = 0; r < W; ++r) sv[j][r] = load_scale<SL>(static_cast<const char*>(a.scales[r]) + s_off, c);
     }
   }
 
-  u32x4* const out = static_cast<u32x4*>(a.out);
+  u32x4* const out = static_cast<u32x4*>(a.out[share]);
   constexpr bool kStage = QRS_STAGE_STORES == 2 || (QRS_STAGE_STORES == 1 && OF == kOutF32);
   __shared__ u32x4 stage[kStage ? QRS_BLOCK * P : 1];
   [[maybe_unused]] const int lane = threadIdx.x & 63;
@@ -286,14 +304,18 @@ hipError_t launch_typed(const ReduceLaunch& l, hipStream_t stream) {
   for (int r = 0; r < kMaxWorld; ++r) {
     a.x[r] = r < W ? static_cast<const u32x4*>(l.x[r]) : nullptr;
     a.scales[r] = r < W ? l.scales[r] : nullptr;
+    a.out[r] = r < l.n_shares ? l.out[r] : nullptr;
   }
-  a.out = l.out;
   a.n_chunks = l.n_elems / kChunk;
+  a.x_share_stride = l.x_share_stride / 16;
+  a.scale_share_stride = l.scale_share_stride;
   const uint64_t per_block = static_cast<uint64_t>(QRS_BLOCK) * QRS_CHUNKS_PER_LANE;
   const uint64_t blocks = (a.n_chunks + per_block - 1) / per_block;
   if (blocks == 0 || blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF>), dim3(static_cast<uint32_t>(blocks)), dim3(QRS_BLOCK), 0,
-                     stream, a);
+  if (l.n_shares != 1 && l.n_shares != W) return hipErrorInvalidValue;
+  if (l.x_share_stride % 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF>), dim3(static_cast<uint32_t>(blocks), l.n_shares), dim3(QRS_BLOCK),
+                     0, stream, a);
   return hipGetLastError();
 }
 

@@ -16,18 +16,28 @@ enum ScaleLayout : int { kScaleF32Group128 = 0, kScaleE8M0Block32 = 1 };
 enum OutFormat : int { kOutF32 = 0, kOutBF16 = 1 };
 
 // One launch of the dequant + rank-ordered reduce over a flat [rows*H]
-// element range. Every slice is contiguous row-major, so element e of the
-// share lives at offset e in every x slice and in the output, and its scale
-// at offset e / G in every scale slice (G divides H).
+// element range per share. Every slice is contiguous row-major, so element e
+// of a share lives at offset e in every x slice and in the output, and its
+// scale at offset e / G in every scale slice (G divides H).
+//
+// n_shares == 1: x[r] / scales[r] point at rank r's slice of this GPU's
+// share, out[0] at the share's output.
+// n_shares == W: x[r] / scales[r] point at rank r's whole [BS, H] input (and
+// its scales) before the all-to-all; share j reads row block j of every
+// rank, found x_share_stride / scale_share_stride bytes further on, and
+// writes out[j].
 struct ReduceLaunch {
   int world_size;          // 2, 4 or 8
   XFormat x_format;
   ScaleLayout scale_layout;
   OutFormat out_format;
-  uint64_t n_elems;        // rows * H, a multiple of 128
+  uint64_t n_elems;        // rows * H per share, a multiple of 128
+  int n_shares;            // 1 or world_size
+  uint64_t x_share_stride;      // bytes between consecutive shares' x row blocks
+  uint64_t scale_share_stride;  // bytes between consecutive shares' scale row blocks
   const void* x[kMaxWorld];
   const void* scales[kMaxWorld];
-  void* out;
+  void* out[kMaxWorld];
 };
 
 hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream);

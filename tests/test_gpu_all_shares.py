@@ -1,0 +1,78 @@
+"""GPU parity of qrs_run_all_shares (the group's whole reduce-scatter on one
+GPU, the all-to-all applied by addressing) against the oracle's all-to-all +
+reduce."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_collective_reduction_amd as qrs
+import workloads
+from gpu_util import assert_parity, empty_out, log, oracle_bits, out_bits
+
+pytestmark = pytest.mark.gpu
+
+MODES = [
+    ("int8", "f32_group128"),
+    ("e4m3fn", "f32_group128"),
+    ("e5m2", "f32_group128"),
+    ("e4m3fn", "e8m0_block32"),
+    ("e5m2", "e8m0_block32"),
+]
+
+
+def _run(wl, xs, ss):
+    p = qrs.plan(wl.world_size, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    dx = [torch.from_numpy(x).cuda() for x in xs]
+    ds = [torch.from_numpy(s).cuda() for s in ss]
+    outs = [empty_out(wl.rows, wl.h, wl.out_dtype).fill_(float("nan")) for _ in range(wl.world_size)]
+    qrs.run_all_shares(p, dx, ds, outs)
+    torch.cuda.synchronize()
+    return [out_bits(o) for o in outs]
+
+
+@pytest.mark.parametrize("x_format,scale_layout", MODES)
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("w", [2, 4, 8])
+def test_all_shares_small(gpu, x_format, scale_layout, out_dtype, w):
+    rows, h = 5, 1152
+    wl = workloads.Workload(
+        "all", w, rows * w, h, x_format, scale_layout, out_dtype,
+        x_dist="int_uniform" if x_format == "int8" else "normal",
+        x_param=127 if x_format == "int8" else 40,
+        scale_lo=-12 if scale_layout == "f32_group128" else 110,
+        scale_hi=2 if scale_layout == "f32_group128" else 140, seed=77 + w,
+    )
+    xs, ss = workloads.generate_full(wl)
+    got = _run(wl, xs, ss)
+    want = oracle.all_shares(xs, ss, x_format, scale_layout, out_dtype)
+    for j in range(w):
+        assert_parity(got[j], oracle_bits(want[j], out_dtype), out_dtype, f"share {j}")
+
+
+def test_all_shares_full_size_sampled(gpu):
+    """The W=8, BS=16384, H=8192 MX group (1 GiB of codes) in the launch the
+    benchmark times; every share checked on 24 sampled rows, all columns."""
+    wl = workloads.CONFIGS["C4"]
+    log("[all_shares] generating 8 x [16384, 8192] inputs")
+    xs, ss = workloads.generate_full(wl)
+    got = _run(wl, xs, ss)
+    rng = np.random.default_rng(4)
+    rows = np.sort(np.concatenate([[0, wl.rows - 1], rng.choice(wl.rows, 22, replace=False)]))
+    for j, (rx, rs) in enumerate(oracle.all_to_all(xs, ss)):
+        want = oracle.reduce_scatter_share([x[rows] for x in rx], [s[rows] for s in rs],
+                                           wl.x_format, wl.scale_layout, wl.out_dtype)
+        assert_parity(got[j][rows], oracle_bits(want, wl.out_dtype), wl.out_dtype, f"share {j}")
+
+
+def test_all_shares_rejects_overlapping_outputs(gpu):
+    wl = workloads.CONFIGS["C2"].with_(bs=4 * 8)
+    p = qrs.plan(4, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    xs = [torch.zeros(wl.bs, wl.h, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    ss = [torch.zeros(wl.bs, wl.h // 128, dtype=torch.float32, device="cuda") for _ in range(4)]
+    big = empty_out(wl.rows * 4, wl.h, wl.out_dtype)
+    outs = [big[0:wl.rows], big[wl.rows:2 * wl.rows], big[0:wl.rows], big[3 * wl.rows:]]
+    with pytest.raises(qrs.QrsError) as ei:
+        qrs.run_all_shares(p, xs, ss, outs)
+    assert ei.value.status == qrs.Status.INVALID_ARG

@@ -140,3 +140,16 @@ def generate(wl: Workload) -> Tuple[List[np.ndarray], List[np.ndarray]]:
         xs.append(x)
         ss.append(s)
     return xs, ss
+
+
+def generate_full(wl: Workload) -> Tuple[List[np.ndarray], List[np.ndarray]]:
+    """Every rank's input BEFORE the all-to-all: x ``[BS, H]`` and scales
+    ``[BS, H/G]`` per rank, same distributions as ``generate``; rank r draws
+    from ``default_rng([seed, r, 1])`` (a stream of its own)."""
+    full = wl.with_(world_size=1)  # shapes: rows == bs
+    xs, ss = [], []
+    for r in range(wl.world_size):
+        rng = np.random.default_rng([wl.seed, r, 1])
+        xs.append(_draw_x(rng, full))
+        ss.append(_draw_scales(rng, full))
+    return xs, ss
