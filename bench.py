@@ -37,7 +37,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published peak
 METRIC = "achieved HBM GB/s and % of peak for dequant+reduce at W=8, H=8192"
-KERNEL_SOURCES = ("quantized_collective_reduction_amd/csrc/qrs_kernels.hip",)
+# Source file of the kernel each op times (a traffic summary is valid only
+# for the source it was measured on).
+KERNEL_SOURCES = {
+    "share": "quantized_collective_reduction_amd/csrc/qrs_kernels.hip",
+    "all_shares": "quantized_collective_reduction_amd/csrc/qrs_kernels.hip",
+    "quantize": "quantized_collective_reduction_amd/csrc/qrs_quantize.hip",
+}
 MALL_BYTES = 256 << 20
 
 
@@ -45,12 +51,9 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest():
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()
+def kernel_source_digest(op):
+    with open(os.path.join(ROOT, KERNEL_SOURCES[op]), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def read_traffic(workload_name, op):
@@ -66,7 +69,7 @@ def read_traffic(workload_name, op):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != kernel_source_digest():
+    if fields.get("kernel_source_sha256") != kernel_source_digest(op):
         log(f"[bench] {path} was taken on another kernel source: traffic = null")
         return None
     try:
@@ -143,7 +146,31 @@ def setup_all_shares(wl, dev, qrs, workloads, torch):
     return alg_bytes, launches, outs, None
 
 
-OPS = {"share": setup_share, "all_shares": setup_all_shares}
+def setup_quantize(wl, dev, qrs, workloads, torch):
+    """Producer-side quantization (qrs_quantize) of one rank's bf16
+    activations [BS, H] into the workload's x format and scale layout."""
+    n = wl.bs * wl.h
+    scale_bytes = n // 128 * 4 if wl.scale_layout == "f32_group128" else n // 32
+    alg_bytes = 2 * n + n + scale_bytes
+    t0 = time.perf_counter()
+    bits = workloads.generate_activations(wl, 0)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    n_sets = max(2, -(-4 * MALL_BYTES // alg_bytes))
+    x0 = torch.from_numpy(bits.view("int16")).view(torch.bfloat16).to(dev)
+    stream = torch.cuda.current_stream(dev)
+    g = 128 if wl.scale_layout == "f32_group128" else 32
+    sdt = torch.float32 if wl.scale_layout == "f32_group128" else torch.uint8
+    launches, outs = [], []
+    for k in range(n_sets):
+        x = x0 if k == 0 else x0.clone()
+        codes = torch.empty((wl.bs, wl.h), dtype=torch.uint8, device=dev)
+        scales = torch.empty((wl.bs, wl.h // g), dtype=sdt, device=dev)
+        launches.append(qrs.QuantizeLaunch(x, codes, scales, wl.x_format, wl.scale_layout, stream=stream))
+        outs.append([codes, scales])
+    return alg_bytes, launches, outs, None
+
+
+OPS = {"share": setup_share, "all_shares": setup_all_shares, "quantize": setup_quantize}
 
 
 def main():
@@ -154,7 +181,8 @@ def main():
     ap.add_argument("--workload", default="C4", help="C1..C5 (default C4: W=8, H=8192, the metric's workload)")
     ap.add_argument("--op", default="share", choices=sorted(OPS),
                     help="share: this GPU's share (the hot path, default); all_shares: every rank's share "
-                         "from the inputs before the all-to-all, in one launch")
+                         "from the inputs before the all-to-all, in one launch; quantize: the producer-side "
+                         "quantization of one rank's bf16 activations [BS, H]")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (cpu_baseline = null)")
     args = ap.parse_args()
 
@@ -237,7 +265,8 @@ def main():
     achieved = alg_bytes / avg_launch_s / 1e9
     value = alg_bytes * args.steps / wall / 1e9
     result = {
-        "metric": METRIC if args.op == "share" else METRIC + " (all W shares in one launch)",
+        "metric": {"share": METRIC, "all_shares": METRIC + " (all W shares in one launch)",
+               "quantize": "achieved HBM GB/s and % of peak for the producer-side quantization"}[args.op],
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -252,7 +281,8 @@ def main():
         "config": {
             "workload": f"{wl.name}: W={wl.world_size} BS={wl.bs} H={wl.h} x={wl.x_format} "
                         f"scales={wl.scale_layout} out={wl.out_dtype}"
-                        + ("" if args.op == "share" else ", all W shares from the pre-all-to-all inputs"),
+                        + {"share": "", "all_shares": ", all W shares from the pre-all-to-all inputs",
+                           "quantize": f", quantize one rank's bf16 [{wl.bs}, {wl.h}]"}[args.op],
             "op": args.op,
             "world_size": wl.world_size,
             "bs": wl.bs,

@@ -155,6 +155,41 @@ qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* con
 qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const void* const* scale_full,
                               void* const* out_shares, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Producer side: quantize bf16 activations into the x codes and scales that
+ * the reduce consumes, in one of the page's modes (page
+ * "aclnnQuantReduceScatter", Constraints: per-token-per-group with 128
+ * columns and fp32 scales, or MX with 32 elements and E8M0 scales). The page
+ * does not say how scales are chosen; this library uses
+ *   MX:        the OCP Microscaling v1.0 conversion -- shared exponent
+ *              floor(log2(amax)) - emax of the element format (8 for E4M3,
+ *              15 for E5M2), limited to [-127, 127]; each element divided by
+ *              the scale (exact), clamped to the largest normal, rounded to
+ *              nearest-even; an all-zero block gets code 0;
+ *   per-group: scale = amax / qmax (qmax = 127, 448 or 57344), codes =
+ *              round-to-nearest-even(clamp(v * (qmax / amax), +-qmax)); the
+ *              scale is kept at or above 2^-126 (then the multiplier is
+ *              2^126), which also covers all-zero groups.
+ * Every step is a single binary32 operation (amax, the per-group division,
+ * the per-element product), so results are deterministic bit for bit.
+ *
+ *   tokens, h   x is [tokens, h] bf16, row-major; tokens > 0; h a multiple
+ *               of 128 in [1024, 8192] (as for qrs_plan).
+ *   x_dtype, scale_layout
+ *               a mode of the page (HIFLOAT8: QRS_ERR_UNSUPPORTED; INT8 with
+ *               E8M0: QRS_ERR_INVALID_ARG).
+ *   x_bf16      DEVICE bf16 [tokens, h], 16-byte aligned, finite values
+ *               (NaN / infinity inputs give unspecified codes).
+ *   x_codes     DEVICE uint8 [tokens, h], 16-byte aligned.
+ *   scales      DEVICE [tokens, h/128] fp32 (4-byte aligned) or [tokens, h/32]
+ *               uint8 E8M0.
+ *   stream      a hipStream_t (NULL = the default stream).
+ *
+ * The three buffers must not overlap. Asynchronous; allocates nothing.
+ */
+qrs_status qrs_quantize(int64_t tokens, int64_t h, qrs_x_dtype x_dtype, qrs_scale_layout scale_layout,
+                        const void* x_bf16, void* x_codes, void* scales, void* stream);
+
 /* Free a plan. NULL is accepted. Plans in use by queued runs may be freed:
  * qrs_run copies what the kernel needs into its launch arguments. */
 qrs_status qrs_plan_destroy(qrs_plan_t plan);

@@ -31,8 +31,10 @@ __all__ = [
     "plan",
     "run",
     "run_all_shares",
+    "quantize",
     "Launch",
     "AllSharesLaunch",
+    "QuantizeLaunch",
     "stream_copy",
     "EXPORTED_SYMBOLS",
 ]
@@ -71,6 +73,7 @@ EXPORTED_SYMBOLS = (
     "qrs_plan",
     "qrs_run",
     "qrs_run_all_shares",
+    "qrs_quantize",
     "qrs_plan_destroy",
     "qrs_plan_shape",
     "qrs_status_string",
@@ -106,6 +109,8 @@ def load_library(path: str = LIB_PATH):
     lib.qrs_run.restype = c_int
     lib.qrs_run_all_shares.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), vp, c_sz, vp]
     lib.qrs_run_all_shares.restype = c_int
+    lib.qrs_quantize.argtypes = [c_i64, c_i64, c_int, c_int, vp, vp, vp, vp]
+    lib.qrs_quantize.restype = c_int
     lib.qrs_plan_destroy.argtypes = [vp]
     lib.qrs_plan_destroy.restype = c_int
     lib.qrs_plan_shape.argtypes = [vp, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]
@@ -238,6 +243,24 @@ def run_all_shares(p: Plan, x_full, scale_full, out_shares, stream=None):
     _check(lib.qrs_run_all_shares(p.handle, xs, ss, os_, None, 0, _stream_handle(stream)))
 
 
+def quantize(x_bf16, x_codes, scales, x_dtype, scale_layout, stream=None):
+    """Producer-side quantization of a bf16 ``[tokens, H]`` device tensor into
+    ``x_codes`` (uint8 ``[tokens, H]``) and ``scales`` (fp32 ``[tokens, H/128]``
+    or uint8 E8M0 ``[tokens, H/32]``)."""
+    lib = load_library()
+    if isinstance(x_bf16, int):
+        raise ValueError("pass tensors (the shape is taken from x_bf16)")
+    tokens, h = x_bf16.shape
+    xd = _enum(x_dtype, _X_NAMES, XDtype)
+    sl = _enum(scale_layout, _SCALE_NAMES, ScaleLayout)
+    n = tokens * h
+    _check_tensor(x_bf16, 2 * n, "x_bf16")
+    _check_tensor(x_codes, n, "x_codes")
+    _check_tensor(scales, n // 128 * 4 if sl == ScaleLayout.F32_GROUP128 else n // 32, "scales")
+    _check(lib.qrs_quantize(tokens, h, int(xd), int(sl), _ptr(x_bf16), _ptr(x_codes), _ptr(scales),
+                            _stream_handle(stream)))
+
+
 class Launch:
     """Arguments for ``run`` marshalled once, for repeated launches of one
     plan on fixed buffers (each call is a single C call: no per-call Python
@@ -294,6 +317,29 @@ class AllSharesLaunch:
 
     def __call__(self):
         status = self._fn(self._handle, self._xs, self._ss, self._os, None, 0, self._stream)
+        if status:
+            _check(status)
+
+
+class QuantizeLaunch:
+    """``quantize`` with its arguments marshalled once."""
+
+    def __init__(self, x_bf16, x_codes, scales, x_dtype, scale_layout, stream=None):
+        lib = load_library()
+        tokens, h = x_bf16.shape
+        self._xd = int(_enum(x_dtype, _X_NAMES, XDtype))
+        self._sl = int(_enum(scale_layout, _SCALE_NAMES, ScaleLayout))
+        n = tokens * h
+        _check_tensor(x_bf16, 2 * n, "x_bf16")
+        _check_tensor(x_codes, n, "x_codes")
+        _check_tensor(scales, n // 128 * 4 if self._sl == ScaleLayout.F32_GROUP128 else n // 32, "scales")
+        self._keep = (x_bf16, x_codes, scales)
+        self._args = (tokens, h, self._xd, self._sl, _ptr(x_bf16), _ptr(x_codes), _ptr(scales),
+                      ctypes.c_void_p(_stream_handle(stream)))
+        self._fn = lib.qrs_quantize
+
+    def __call__(self):
+        status = self._fn(*self._args)
         if status:
             _check(status)
 

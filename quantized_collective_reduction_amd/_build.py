@@ -19,7 +19,11 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(REPO_ROOT, "include")
 LIB_NAME = "libqrs.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = [os.path.join(CSRC, "qrs.cpp"), os.path.join(CSRC, "qrs_kernels.hip")]
+SOURCES = [
+    os.path.join(CSRC, "qrs.cpp"),
+    os.path.join(CSRC, "qrs_kernels.hip"),
+    os.path.join(CSRC, "qrs_quantize.hip"),
+]
 
 BASE_FLAGS = [
     "--offload-arch=gfx950",

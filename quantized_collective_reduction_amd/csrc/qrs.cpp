@@ -46,6 +46,27 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// The (x format, scale layout) pair selects one of the page's modes.
+qrs_status check_mode(qrs_x_dtype x_dtype, qrs_scale_layout scale_layout) {
+  if (x_dtype == QRS_X_HIFLOAT8)
+    return fail(QRS_ERR_UNSUPPORTED, "HIFLOAT8 x is reserved: its encoding is not defined");
+  if (x_dtype != QRS_X_INT8 && x_dtype != QRS_X_FP8_E4M3FN && x_dtype != QRS_X_FP8_E5M2)
+    return fail(QRS_ERR_INVALID_ARG, "x_dtype %d is not a qrs_x_dtype", static_cast<int>(x_dtype));
+  if (scale_layout != QRS_SCALE_F32_GROUP128 && scale_layout != QRS_SCALE_E8M0_BLOCK32)
+    return fail(QRS_ERR_INVALID_ARG, "scale_layout %d is not a qrs_scale_layout", static_cast<int>(scale_layout));
+  // MX mode (E8M0 scales) is defined for the FP8 formats only.
+  if (scale_layout == QRS_SCALE_E8M0_BLOCK32 && x_dtype == QRS_X_INT8)
+    return fail(QRS_ERR_INVALID_ARG, "INT8 x is paired with fp32 per-group scales only");
+  return QRS_OK;
+}
+
+// H is 128-aligned and in [1024, 8192].
+bool valid_h(int64_t h) { return h >= 1024 && h <= 8192 && h % 128 == 0; }
+
+qrs::XFormat to_x_format(qrs_x_dtype x) {
+  return x == QRS_X_INT8 ? qrs::kXInt8 : x == QRS_X_FP8_E4M3FN ? qrs::kXE4M3FN : qrs::kXE5M2;
+}
+
 }  // namespace
 
 extern "C" {
@@ -75,21 +96,14 @@ qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, 
     return fail(QRS_ERR_INVALID_ARG, "bs %lld is not a multiple of world_size %d", static_cast<long long>(bs),
                 world_size);
   // H is 128-aligned and in [1024, 8192].
-  if (h < 1024 || h > 8192 || h % 128 != 0)
+  if (!valid_h(h))
     return fail(QRS_ERR_INVALID_ARG, "h %lld: must be a multiple of 128 in [1024, 8192]", static_cast<long long>(h));
   const int64_t rows = bs / world_size;
   // rows * h elements, each a 16-element chunk per lane; keep the launch in range.
   if (rows > (int64_t{1} << 40) / h) return fail(QRS_ERR_INVALID_ARG, "bs %lld too large", static_cast<long long>(bs));
 
-  if (x_dtype == QRS_X_HIFLOAT8)
-    return fail(QRS_ERR_UNSUPPORTED, "HIFLOAT8 x is reserved: its encoding is not defined");
-  if (x_dtype != QRS_X_INT8 && x_dtype != QRS_X_FP8_E4M3FN && x_dtype != QRS_X_FP8_E5M2)
-    return fail(QRS_ERR_INVALID_ARG, "x_dtype %d is not a qrs_x_dtype", static_cast<int>(x_dtype));
-  if (scale_layout != QRS_SCALE_F32_GROUP128 && scale_layout != QRS_SCALE_E8M0_BLOCK32)
-    return fail(QRS_ERR_INVALID_ARG, "scale_layout %d is not a qrs_scale_layout", static_cast<int>(scale_layout));
-  // MX mode (E8M0 scales) is defined for the FP8 formats only.
-  if (scale_layout == QRS_SCALE_E8M0_BLOCK32 && x_dtype == QRS_X_INT8)
-    return fail(QRS_ERR_INVALID_ARG, "INT8 x is paired with fp32 per-group scales only");
+  const qrs_status mode = check_mode(x_dtype, scale_layout);
+  if (mode != QRS_OK) return mode;
   if (out_dtype != QRS_OUT_F32 && out_dtype != QRS_OUT_BF16)
     return fail(QRS_ERR_INVALID_ARG, "out_dtype %d is not a qrs_out_dtype", static_cast<int>(out_dtype));
 
@@ -99,7 +113,7 @@ qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, 
   p->bs = bs;
   p->rows = rows;
   p->h = h;
-  p->x_format = x_dtype == QRS_X_INT8 ? qrs::kXInt8 : x_dtype == QRS_X_FP8_E4M3FN ? qrs::kXE4M3FN : qrs::kXE5M2;
+  p->x_format = to_x_format(x_dtype);
   p->scale_layout = scale_layout == QRS_SCALE_F32_GROUP128 ? qrs::kScaleF32Group128 : qrs::kScaleE8M0Block32;
   p->out_format = out_dtype == QRS_OUT_F32 ? qrs::kOutF32 : qrs::kOutBF16;
   *plan_out = p;
@@ -200,6 +214,37 @@ qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const 
     l.scales[r] = scale_full[r];
   }
   const hipError_t e = qrs::launch_reduce(l, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qrs_status qrs_quantize(int64_t tokens, int64_t h, qrs_x_dtype x_dtype, qrs_scale_layout scale_layout,
+                        const void* x_bf16, void* x_codes, void* scales, void* stream) {
+  if (tokens <= 0) return fail(QRS_ERR_INVALID_ARG, "tokens %lld: must be positive", static_cast<long long>(tokens));
+  if (!valid_h(h))
+    return fail(QRS_ERR_INVALID_ARG, "h %lld: must be a multiple of 128 in [1024, 8192]", static_cast<long long>(h));
+  if (tokens > (int64_t{1} << 40) / h)
+    return fail(QRS_ERR_INVALID_ARG, "tokens %lld too large", static_cast<long long>(tokens));
+  const qrs_status mode = check_mode(x_dtype, scale_layout);
+  if (mode != QRS_OK) return mode;
+  if (!x_bf16 || !x_codes || !scales) return fail(QRS_ERR_INVALID_ARG, "null pointer");
+  const bool f32_scales = scale_layout == QRS_SCALE_F32_GROUP128;
+  if (!aligned(x_bf16, 16)) return fail(QRS_ERR_INVALID_ARG, "input is not 16-byte aligned");
+  if (!aligned(x_codes, 16)) return fail(QRS_ERR_INVALID_ARG, "codes output is not 16-byte aligned");
+  if (f32_scales && !aligned(scales, 4)) return fail(QRS_ERR_INVALID_ARG, "fp32 scales are not 4-byte aligned");
+  const uint64_t n = static_cast<uint64_t>(tokens) * static_cast<uint64_t>(h);
+  const uint64_t scale_bytes = f32_scales ? n / 128 * 4 : n / 32;
+  if (overlaps(x_bf16, 2 * n, x_codes, n) || overlaps(x_bf16, 2 * n, scales, scale_bytes) ||
+      overlaps(x_codes, n, scales, scale_bytes))
+    return fail(QRS_ERR_INVALID_ARG, "input, codes and scales must not overlap");
+  qrs::QuantizeLaunch l;
+  l.x_format = to_x_format(x_dtype);
+  l.scale_layout = f32_scales ? qrs::kScaleF32Group128 : qrs::kScaleE8M0Block32;
+  l.n_elems = n;
+  l.in = x_bf16;
+  l.codes = x_codes;
+  l.scales = scales;
+  const hipError_t e = qrs::launch_quantize(l, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

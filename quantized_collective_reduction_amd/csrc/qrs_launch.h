@@ -42,6 +42,20 @@ struct ReduceLaunch {
 
 hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream);
 
+// Producer-side quantization of n_elems bf16 values (a multiple of 128,
+// row-major [tokens, H] with G dividing H, so groups never cross rows):
+// codes (uint8, one per element) and scales (fp32 per 128 or E8M0 per 32).
+struct QuantizeLaunch {
+  XFormat x_format;
+  ScaleLayout scale_layout;
+  uint64_t n_elems;
+  const void* in;  // bf16, 16-byte aligned
+  void* codes;     // 8-byte aligned
+  void* scales;    // 4-byte aligned for fp32
+};
+
+hipError_t launch_quantize(const QuantizeLaunch& l, hipStream_t stream);
+
 // Plain 16-byte-per-lane device copy (bytes % 16 == 0, both pointers 16-byte
 // aligned): the reference stream for bandwidth and traffic-counter
 // calibration.

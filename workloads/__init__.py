@@ -153,3 +153,18 @@ def generate_full(wl: Workload) -> Tuple[List[np.ndarray], List[np.ndarray]]:
         xs.append(_draw_x(rng, full))
         ss.append(_draw_scales(rng, full))
     return xs, ss
+
+
+def generate_activations(wl: Workload, r: int, tokens: int = None) -> np.ndarray:
+    """Rank r's bf16 activations ``[tokens, H]`` (default tokens = BS) as
+    uint16 bit patterns, for the producer-side quantization: N(0,1) values
+    times a per-token power of two drawn uniformly from 2^-8 .. 2^8, encoded
+    by torch's nearest-even float32 -> bf16 cast. Stream
+    ``default_rng([seed, r, 2])``."""
+    import torch
+
+    t = wl.bs if tokens is None else tokens
+    rng = np.random.default_rng([wl.seed, r, 2])
+    v = rng.standard_normal(size=(t, wl.h)).astype(np.float32)
+    v *= np.exp2(rng.integers(-8, 9, size=(t, 1))).astype(np.float32)
+    return torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
