@@ -13,6 +13,7 @@
  *     acc      = p_0;  acc = fp32(acc + p_r)  for r = 1 .. W-1, in rank order
  *     out[i][c] = acc                 (QRS_OUT_F32)
  *     out[i][c] = bf16_rne(acc)       (QRS_OUT_BF16)
+ *     out[i][c] = f16_rne(acc)        (QRS_OUT_F16)
  *
  * Products and sums are separate binary32 operations rounded to nearest-even
  * (no fused multiply-add), subnormals are kept, NaN and infinity propagate.
@@ -73,9 +74,15 @@ typedef enum qrs_scale_layout {
   QRS_SCALE_E8M0_BLOCK32 = 1
 } qrs_scale_layout;
 
+/* Output type. The page's output dtype table did not survive extraction;
+ * fp32 and bf16 are the types the workloads use, fp16 is the other 16-bit
+ * output a half-precision consumer takes. Both 16-bit types are the
+ * round-to-nearest-even of the fp32 accumulator (fp16: values from 65520 up
+ * become infinity, subnormals are kept). */
 typedef enum qrs_out_dtype {
-  QRS_OUT_F32 = 0, /* float32 [rows, H]                                 */
-  QRS_OUT_BF16 = 1 /* bfloat16 [rows, H], round-to-nearest-even of fp32 */
+  QRS_OUT_F32 = 0,  /* float32 [rows, H]                                 */
+  QRS_OUT_BF16 = 1, /* bfloat16 [rows, H], round-to-nearest-even of fp32 */
+  QRS_OUT_F16 = 2   /* IEEE binary16 [rows, H], round-to-nearest-even    */
 } qrs_out_dtype;
 
 typedef struct qrs_plan_s* qrs_plan_t;
@@ -154,6 +161,30 @@ qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* con
  */
 qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const void* const* scale_full,
                               void* const* out_shares, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * qrs_run for slices and an output whose rows are not adjacent: row i of
+ * rank r's x slice starts i * x_row_stride bytes after x_slices[r], row i of
+ * its scales i * scale_row_stride scale elements after scale_slices[r], and
+ * row i of the output i * out_row_stride output elements after out. This
+ * covers slices that are row ranges of wider buffers (for example a column
+ * range [.., c0:c0+H] of a [BS, H_total] tensor) and padded rows. Same
+ * arithmetic and result as qrs_run on the same values.
+ *
+ *   x_row_stride      bytes, >= h, a multiple of 16 (rows stay 16-byte
+ *                     aligned; x_slices[r] 16-byte aligned).
+ *   scale_row_stride  elements, >= h / G (fp32 scale pointers 4-byte
+ *                     aligned).
+ *   out_row_stride    elements, >= h, spanning a multiple of 16 bytes; out
+ *                     16-byte aligned.
+ *
+ * The output's address span, from its first to the last element written,
+ * must not overlap the address span of any input slice. Errors as for
+ * qrs_run.
+ */
+qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t x_row_stride,
+                           const void* const* scale_slices, int64_t scale_row_stride, void* out,
+                           int64_t out_row_stride, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Producer side: quantize bf16 activations into the x codes and scales that

@@ -48,6 +48,7 @@ from .reduce import (
     dequantize_rank,
     reduce_scatter_share,
     fp32_to_bf16_bits,
+    fp32_to_f16_bits,
     bf16_bits_to_fp32,
 )
 
@@ -63,5 +64,6 @@ __all__ = [
     "dequantize_rank",
     "reduce_scatter_share",
     "fp32_to_bf16_bits",
+    "fp32_to_f16_bits",
     "bf16_bits_to_fp32",
 ]

@@ -26,7 +26,7 @@ import numpy as np
 
 X_FORMATS = ("int8", "e4m3fn", "e5m2")
 SCALE_LAYOUTS = ("f32_group128", "e8m0_block32")
-OUT_DTYPES = ("f32", "bf16")
+OUT_DTYPES = ("f32", "bf16", "f16")
 
 # Elements of one row that share one scale, per scale layout.
 GROUP_SIZE = {"f32_group128": 128, "e8m0_block32": 32}

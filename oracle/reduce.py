@@ -16,6 +16,7 @@ the per-token-per-group mode, 32 in the MX mode, Constraints):
     acc     = fp32( acc + p_r )            for r = 1 .. W-1, in that order
     Y[i, c] = acc                          fp32 output
     Y[i, c] = bf16_rne(acc)                bf16 output
+    Y[i, c] = f16_rne(acc)                 fp16 output
 
 Readings of what the page leaves open (each is listed with its reason in the
 design notes): the reduction is a left fold in rank order 0..W-1; the fold
@@ -90,6 +91,34 @@ def fp32_to_bf16_bits(acc):
     return np.where(is_nan, quiet, rounded).astype(np.uint16)
 
 
+def fp32_to_f16_bits(acc):
+    """Round binary32 values to IEEE binary16 (nearest, ties to even); uint16
+    bits. binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits; normals
+    from 2^-14, subnormal quantum 2^-24, largest finite 65504.
+
+    Written out: in float64 (which holds every binary32 value and every
+    quotient below exactly) take the binade E = floor(log2 |v|), the quantum
+    2^(max(E, -14) - 10) of binary16 at that magnitude, round |v| / quantum
+    to the nearest integer with ties to even, and multiply back. A result
+    above 65504 (that is, |v| >= 65520) is infinity. NaN maps to a quiet NaN
+    of the same sign.
+    """
+    v = np.ascontiguousarray(acc, dtype=np.float32).astype(np.float64)
+    a = np.abs(v)
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        _, e2 = np.frexp(a)  # a = m * 2^e2, m in [0.5, 1)
+        binade = np.maximum(e2 - 1, -14)
+        quantum = np.ldexp(1.0, binade - 10)
+        r = np.rint(a / quantum) * quantum  # exact scaling, RNE to an integer
+        r = np.where(r > 65504.0, np.inf, r)
+        r = np.where(np.isinf(a), np.inf, r)
+    mag = np.where(np.isnan(a), 0.0, r).astype(np.float16)  # exact: r is a binary16 value or inf
+    bits = mag.view(np.uint16)
+    sign = (np.signbit(v).astype(np.uint16) << 15).astype(np.uint16)
+    nan_bits = (np.uint16(0x7E00) | sign).astype(np.uint16)
+    return np.where(np.isnan(v), nan_bits, bits | sign).astype(np.uint16)
+
+
 def bf16_bits_to_fp32(bits):
     """Widen bf16 bit patterns (uint16) to float32 values (exact)."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
@@ -102,13 +131,14 @@ def reduce_scatter_share(x_slices, scale_slices, x_format, scale_layout, out_dty
     ``x_slices[r]``: uint8 ``[rows, H]`` codes from rank r, r = 0..W-1.
     ``scale_slices[r]``: that rank's scales (layout as in ``dequantize_rank``).
     Returns float32 ``[rows, H]`` for ``out_dtype == "f32"`` and the uint16
-    bit patterns of bf16 ``[rows, H]`` for ``out_dtype == "bf16"``.
+    bit patterns of bf16 or binary16 ``[rows, H]`` for ``out_dtype`` "bf16"
+    or "f16".
     """
     if x_format not in ("int8", "e4m3fn", "e5m2"):
         raise ValueError(f"unknown x format {x_format!r}")
     if scale_layout not in GROUP_SIZE:
         raise ValueError(f"unknown scale layout {scale_layout!r}")
-    if out_dtype not in ("f32", "bf16"):
+    if out_dtype not in ("f32", "bf16", "f16"):
         raise ValueError(f"unknown output dtype {out_dtype!r}")
     _check_shapes(x_slices, scale_slices, scale_layout)
 
@@ -120,6 +150,8 @@ def reduce_scatter_share(x_slices, scale_slices, x_format, scale_layout, out_dty
     assert acc.dtype == np.float32
     if out_dtype == "f32":
         return acc
+    if out_dtype == "f16":
+        return fp32_to_f16_bits(acc)
     return fp32_to_bf16_bits(acc)
 
 

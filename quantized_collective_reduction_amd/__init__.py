@@ -31,6 +31,7 @@ __all__ = [
     "plan",
     "run",
     "run_all_shares",
+    "run_strided",
     "quantize",
     "Launch",
     "AllSharesLaunch",
@@ -62,17 +63,19 @@ class ScaleLayout(IntEnum):
 class OutDtype(IntEnum):
     F32 = 0
     BF16 = 1
+    F16 = 2
 
 
 _X_NAMES = {"int8": XDtype.INT8, "e4m3fn": XDtype.FP8_E4M3FN, "e5m2": XDtype.FP8_E5M2, "hifloat8": XDtype.HIFLOAT8}
 _SCALE_NAMES = {"f32_group128": ScaleLayout.F32_GROUP128, "e8m0_block32": ScaleLayout.E8M0_BLOCK32}
-_OUT_NAMES = {"f32": OutDtype.F32, "bf16": OutDtype.BF16}
+_OUT_NAMES = {"f32": OutDtype.F32, "bf16": OutDtype.BF16, "f16": OutDtype.F16}
 
 # Every function include/qrs.h declares.
 EXPORTED_SYMBOLS = (
     "qrs_plan",
     "qrs_run",
     "qrs_run_all_shares",
+    "qrs_run_strided",
     "qrs_quantize",
     "qrs_plan_destroy",
     "qrs_plan_shape",
@@ -109,6 +112,8 @@ def load_library(path: str = LIB_PATH):
     lib.qrs_run.restype = c_int
     lib.qrs_run_all_shares.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), vp, c_sz, vp]
     lib.qrs_run_all_shares.restype = c_int
+    lib.qrs_run_strided.argtypes = [vp, ctypes.POINTER(vp), c_i64, ctypes.POINTER(vp), c_i64, vp, c_i64, vp, c_sz, vp]
+    lib.qrs_run_strided.restype = c_int
     lib.qrs_quantize.argtypes = [c_i64, c_i64, c_int, c_int, vp, vp, vp, vp]
     lib.qrs_quantize.restype = c_int
     lib.qrs_plan_destroy.argtypes = [vp]
@@ -219,6 +224,40 @@ def run(p: Plan, x_slices, scale_slices, out, stream=None):
     xs = (ctypes.c_void_p * w)(*[_ptr(t) for t in x_slices])
     ss = (ctypes.c_void_p * w)(*[_ptr(t) for t in scale_slices])
     _check(lib.qrs_run(p.handle, xs, ss, _ptr(out), None, 0, _stream_handle(stream)))
+
+
+def _row_stride(tensors, rows, cols, what):
+    """Common row stride (in elements) of 2-D device views [rows, cols] whose
+    elements within a row are adjacent."""
+    strides = set()
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("device tensors only (there is no CPU path)")
+        if t.dim() != 2 or tuple(t.shape) != (rows, cols):
+            raise ValueError(f"{what}: expected shape [{rows}, {cols}], got {list(t.shape)}")
+        if t.stride(1) != 1 and cols > 1:
+            raise ValueError(f"{what}: elements within a row must be adjacent")
+        strides.add(t.stride(0) if rows > 1 else cols)
+    if len(strides) != 1:
+        raise ValueError(f"{what}: every slice must have the same row stride")
+    return strides.pop()
+
+
+def run_strided(p: Plan, x_slices, scale_slices, out, stream=None):
+    """``run`` for 2-D views whose rows are not adjacent (row ranges of wider
+    buffers, padded rows): x slices ``[rows, H]`` uint8, scale slices
+    ``[rows, H/G]``, out ``[rows, H]``; each kind shares one row stride."""
+    lib = load_library()
+    w = p.world_size
+    if len(x_slices) != w or len(scale_slices) != w:
+        raise ValueError(f"need {w} x slices and {w} scale slices")
+    ld_x = _row_stride(x_slices, p.rows, p.h, "x slices")
+    ld_s = _row_stride(scale_slices, p.rows, p.h // p.group, "scale slices")
+    ld_o = _row_stride([out], p.rows, p.h, "out")
+    xs = (ctypes.c_void_p * w)(*[t.data_ptr() for t in x_slices])
+    ss = (ctypes.c_void_p * w)(*[t.data_ptr() for t in scale_slices])
+    _check(lib.qrs_run_strided(p.handle, xs, ld_x * x_slices[0].element_size(), ss, ld_s, out.data_ptr(), ld_o,
+                               None, 0, _stream_handle(stream)))
 
 
 def run_all_shares(p: Plan, x_full, scale_full, out_shares, stream=None):

@@ -104,7 +104,7 @@ qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, 
 
   const qrs_status mode = check_mode(x_dtype, scale_layout);
   if (mode != QRS_OK) return mode;
-  if (out_dtype != QRS_OUT_F32 && out_dtype != QRS_OUT_BF16)
+  if (out_dtype != QRS_OUT_F32 && out_dtype != QRS_OUT_BF16 && out_dtype != QRS_OUT_F16)
     return fail(QRS_ERR_INVALID_ARG, "out_dtype %d is not a qrs_out_dtype", static_cast<int>(out_dtype));
 
   qrs_plan_s* p = new (std::nothrow) qrs_plan_s;
@@ -115,7 +115,7 @@ qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, 
   p->h = h;
   p->x_format = to_x_format(x_dtype);
   p->scale_layout = scale_layout == QRS_SCALE_F32_GROUP128 ? qrs::kScaleF32Group128 : qrs::kScaleE8M0Block32;
-  p->out_format = out_dtype == QRS_OUT_F32 ? qrs::kOutF32 : qrs::kOutBF16;
+  p->out_format = out_dtype == QRS_OUT_F32 ? qrs::kOutF32 : out_dtype == QRS_OUT_BF16 ? qrs::kOutBF16 : qrs::kOutF16;
   *plan_out = p;
   *workspace_bytes_out = 0;
   return ok();
@@ -152,7 +152,8 @@ qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* con
   l.x_format = plan->x_format;
   l.scale_layout = plan->scale_layout;
   l.out_format = plan->out_format;
-  l.n_elems = n;
+  l.n_rows = 1;
+  l.row_elems = n;
   l.n_shares = 1;
   l.out[0] = out;
   for (int r = 0; r < W; ++r) {
@@ -189,7 +190,8 @@ qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const 
   l.x_format = plan->x_format;
   l.scale_layout = plan->scale_layout;
   l.out_format = plan->out_format;
-  l.n_elems = n;
+  l.n_rows = 1;
+  l.row_elems = n;
   l.n_shares = W;
   l.x_share_stride = n;  // row block j of rank r starts j * rows * H bytes into x_full[r]
   l.scale_share_stride = share_scale_bytes;
@@ -212,6 +214,64 @@ qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const 
         return fail(QRS_ERR_INVALID_ARG, "output of share %d overlaps an input of rank %d", j, r);
     l.x[r] = x_full[r];
     l.scales[r] = scale_full[r];
+  }
+  const hipError_t e = qrs::launch_reduce(l, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t x_row_stride,
+                           const void* const* scale_slices, int64_t scale_row_stride, void* out,
+                           int64_t out_row_stride, void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!plan) return fail(QRS_ERR_INVALID_ARG, "null plan");
+  if (!x_slices || !scale_slices || !out) return fail(QRS_ERR_INVALID_ARG, "null pointer array or output");
+  const int W = plan->world_size;
+  const int64_t rows = plan->rows, h = plan->h;
+  const bool f32_scales = plan->scale_layout == qrs::kScaleF32Group128;
+  const int64_t g = f32_scales ? 128 : 32;
+  const int64_t sb = f32_scales ? 4 : 1;
+  const int64_t ob = plan->out_format == qrs::kOutF32 ? 4 : 2;
+  if (x_row_stride < h || x_row_stride % 16)
+    return fail(QRS_ERR_INVALID_ARG, "x_row_stride %lld: must be >= h and a multiple of 16 bytes",
+                static_cast<long long>(x_row_stride));
+  if (scale_row_stride < h / g)
+    return fail(QRS_ERR_INVALID_ARG, "scale_row_stride %lld: must be >= h / %lld", static_cast<long long>(scale_row_stride),
+                static_cast<long long>(g));
+  if (out_row_stride < h || (out_row_stride * ob) % 16)
+    return fail(QRS_ERR_INVALID_ARG, "out_row_stride %lld: must be >= h and span a multiple of 16 bytes",
+                static_cast<long long>(out_row_stride));
+  if (x_row_stride > (int64_t{1} << 40) || scale_row_stride > (int64_t{1} << 40) || out_row_stride > (int64_t{1} << 40))
+    return fail(QRS_ERR_INVALID_ARG, "row stride too large");
+  if (!aligned(out, 16)) return fail(QRS_ERR_INVALID_ARG, "out is not 16-byte aligned");
+  // Extents actually addressed (last row ends at its h-th element).
+  const uint64_t x_span = static_cast<uint64_t>((rows - 1) * x_row_stride + h);
+  const uint64_t s_span = static_cast<uint64_t>(((rows - 1) * scale_row_stride + h / g) * sb);
+  const uint64_t o_span = static_cast<uint64_t>(((rows - 1) * out_row_stride + h) * ob);
+
+  qrs::ReduceLaunch l;
+  std::memset(&l, 0, sizeof(l));
+  l.world_size = W;
+  l.x_format = plan->x_format;
+  l.scale_layout = plan->scale_layout;
+  l.out_format = plan->out_format;
+  l.n_rows = static_cast<uint64_t>(rows);
+  l.row_elems = static_cast<uint64_t>(h);
+  l.x_row_stride = static_cast<uint64_t>(x_row_stride);
+  l.scale_row_stride = static_cast<uint64_t>(scale_row_stride * sb);
+  l.out_row_stride = static_cast<uint64_t>(out_row_stride * ob);
+  l.n_shares = 1;
+  l.out[0] = out;
+  for (int r = 0; r < W; ++r) {
+    if (!x_slices[r] || !scale_slices[r]) return fail(QRS_ERR_INVALID_ARG, "null slice pointer for rank %d", r);
+    if (!aligned(x_slices[r], 16)) return fail(QRS_ERR_INVALID_ARG, "x slice of rank %d is not 16-byte aligned", r);
+    if (f32_scales && !aligned(scale_slices[r], 4))
+      return fail(QRS_ERR_INVALID_ARG, "fp32 scale slice of rank %d is not 4-byte aligned", r);
+    if (overlaps(out, o_span, x_slices[r], x_span) || overlaps(out, o_span, scale_slices[r], s_span))
+      return fail(QRS_ERR_INVALID_ARG, "out overlaps an input slice of rank %d", r);
+    l.x[r] = x_slices[r];
+    l.scales[r] = scale_slices[r];
   }
   const hipError_t e = qrs::launch_reduce(l, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -74,6 +74,7 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kChunk = 16;  // elements per chunk: one 16-byte load of codes
 
@@ -144,7 +145,14 @@ struct KernelArgs {
   const u32x4* x[kMaxWorld];
   const void* scales[kMaxWorld];
   void* out[kMaxWorld];  // one per share (blockIdx.y)
-  uint64_t n_chunks;     // chunks per share
+  // The share is n_rows rows of chunks_per_row chunks; a row is covered by
+  // blocks_per_row consecutive blocks. Contiguous shares are one row of all
+  // their chunks (row strides unused).
+  uint64_t chunks_per_row;
+  uint32_t blocks_per_row;
+  uint64_t x_row_stride;      // in 16-byte units
+  uint64_t scale_row_stride;  // in bytes
+  uint64_t out_row_stride;    // in 16-byte units
   uint64_t x_share_stride;      // in 16-byte units
   uint64_t scale_share_stride;  // in bytes
 };
@@ -196,7 +204,7 @@ __device__ __forceinline__ void fold_chunk(const u32x4 (&xv)[W], const float (&s
   }
 }
 
-// The chunk's output as 16-byte pieces: 4 for fp32, 2 for bf16.
+// The chunk's output as 16-byte pieces: 4 for fp32, 2 for bf16 and fp16.
 template <int OF>
 struct OutPieces {
   static constexpr int kCount = OF == kOutF32 ? 4 : 2;
@@ -217,38 +225,53 @@ __device__ __forceinline__ void pack_chunk(const float (&acc)[kChunk], u32x4 (&p
       f32x2 pr;
       pr.x = acc[2 * k];
       pr.y = acc[2 * k + 1];
-      // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN.
-      packed[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+      if constexpr (OF == kOutBF16) {
+        // v_cvt_pk_bf16_f32: round to nearest even, NaN stays NaN.
+        packed[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+      } else {
+        // v_cvt_pk_f16_f32: round to nearest even, overflow to infinity.
+        packed[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, f16x2));
+      }
     }
     piece[0] = u32x4{packed[0], packed[1], packed[2], packed[3]};
     piece[1] = u32x4{packed[4], packed[5], packed[6], packed[7]};
   }
 }
 
-template <int W, int XF, int SL, int OF>
+// Addressing of a launch: one contiguous share (no per-block offset
+// arithmetic: the hot path), one share with row-strided slices and output,
+// or all W shares of contiguous pre-all-to-all inputs (blockIdx.y = share).
+enum Addr : int { kAddrFlat = 0, kAddrRows = 1, kAddrShares = 2 };
+
+template <int W, int XF, int SL, int OF, int ADDR>
 __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
+  constexpr bool ROWS = ADDR == kAddrRows;
+  constexpr bool SHARES = ADDR == kAddrShares;
   constexpr int CH = QRS_CHUNKS_PER_LANE;
   constexpr int P = OutPieces<OF>::kCount;
-  // Chunk j of this lane is base + j*QRS_BLOCK: every load instruction of a
-  // wave covers one contiguous range.
   uint32_t block_id = blockIdx.x;
 #if QRS_XCD_REMAP
   if ((gridDim.x & 7u) == 0) block_id = (block_id & 7u) * (gridDim.x >> 3) + (block_id >> 3);
 #endif
-  const uint64_t block_first = static_cast<uint64_t>(block_id) * (QRS_BLOCK * CH);
+  // Row and first chunk of this block (uniform). Chunk j of this lane is
+  // base + j*QRS_BLOCK within the row: every load instruction of a wave
+  // covers one contiguous range.
+  const uint32_t row = ROWS ? block_id / a.blocks_per_row : 0u;
+  const uint64_t block_first = static_cast<uint64_t>(block_id - row * a.blocks_per_row) * (QRS_BLOCK * CH);
   const uint64_t base = block_first + threadIdx.x;
+  const uint64_t n_chunks = a.chunks_per_row;
   // Share handled by this block (one share unless the all-to-all is
   // emulated on this GPU): uniform offsets into every rank's input.
-  const uint32_t share = blockIdx.y;
-  const uint64_t x_off = share * a.x_share_stride;
-  const uint64_t s_off = share * a.scale_share_stride;
+  const uint32_t share = SHARES ? blockIdx.y : 0u;
+  const uint64_t x_off = (SHARES ? share * a.x_share_stride : 0) + (ROWS ? row * a.x_row_stride : 0);
+  const uint64_t s_off = (SHARES ? share * a.scale_share_stride : 0) + (ROWS ? row * a.scale_row_stride : 0);
 
   u32x4 xv[CH][W];
   float sv[CH][W];
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
     const uint64_t c = base + static_cast<uint64_t>(j) * QRS_BLOCK;
-    if (c < a.n_chunks) {
+    if (c < n_chunks) {
 #pragma unroll
       for (int r = 0; r < W; ++r) xv[j][r] = load_stream(a.x[r] + x_off + c);
 #pragma unroll
@@ -256,7 +279,7 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
     }
   }
 
-  u32x4* const out = static_cast<u32x4*>(a.out[share]);
+  u32x4* const out = static_cast<u32x4*>(a.out[share]) + (ROWS ? row * a.out_row_stride : 0);
   constexpr bool kStage = QRS_STAGE_STORES == 2 || (QRS_STAGE_STORES == 1 && OF == kOutF32);
   __shared__ u32x4 stage[kStage ? QRS_BLOCK * P : 1];
   [[maybe_unused]] const int lane = threadIdx.x & 63;
@@ -266,7 +289,7 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
   for (int j = 0; j < CH; ++j) {
     const uint64_t c = base + static_cast<uint64_t>(j) * QRS_BLOCK;
     u32x4 piece[P];
-    if (c < a.n_chunks) {
+    if (c < n_chunks) {
       float acc[kChunk];
       fold_chunk<W, XF>(xv[j], sv[j], acc);
       pack_chunk<OF>(acc, piece);
@@ -276,11 +299,11 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
       }
     }
     if constexpr (kStage) {
-      // The wave's 64 chunks are contiguous in the output: write them to LDS
-      // in output order, then let lane l store pieces l, l+64, ... of that
-      // range, so each store instruction covers 64 consecutive pieces.
+      // The wave's 64 chunks are contiguous in the output row: write them to
+      // LDS in output order, then let lane l store pieces l, l+64, ... of
+      // that range, so each store instruction covers 64 consecutive pieces.
       if (j > 0) stage_sync();  // the previous round's reads are done
-      if (c < a.n_chunks) {
+      if (c < n_chunks) {
 #pragma unroll
         for (int q = 0; q < P; ++q) wave_stage[lane * P + q] = piece[q];
       }
@@ -292,7 +315,7 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
 #pragma unroll
       for (int q = 0; q < P; ++q) {
         const int k = q * 64 + lane;  // piece k of the wave's range belongs to chunk k / P
-        if (wave_first_chunk + k / P < a.n_chunks) store_stream(out + wave_first_chunk * P + k, staged[q]);
+        if (wave_first_chunk + k / P < n_chunks) store_stream(out + wave_first_chunk * P + k, staged[q]);
       }
     }
   }
@@ -306,22 +329,40 @@ hipError_t launch_typed(const ReduceLaunch& l, hipStream_t stream) {
     a.scales[r] = r < W ? l.scales[r] : nullptr;
     a.out[r] = r < l.n_shares ? l.out[r] : nullptr;
   }
-  a.n_chunks = l.n_elems / kChunk;
+  if (l.n_rows == 0 || l.row_elems == 0 || l.row_elems % 128) return hipErrorInvalidValue;
+  if (l.x_row_stride % 16 || l.out_row_stride % 16 || l.x_share_stride % 16) return hipErrorInvalidValue;
+  if (l.n_shares != 1 && l.n_shares != W) return hipErrorInvalidValue;
+  a.chunks_per_row = l.row_elems / kChunk;
+  const uint64_t per_block = static_cast<uint64_t>(QRS_BLOCK) * QRS_CHUNKS_PER_LANE;
+  const uint64_t bpr = (a.chunks_per_row + per_block - 1) / per_block;
+  const uint64_t blocks = bpr * l.n_rows;
+  if (bpr > 0xFFFFFFFFull || blocks > 0x7FFFFFFFull || l.n_rows > 0xFFFFFFFFull) return hipErrorInvalidValue;
+  a.blocks_per_row = static_cast<uint32_t>(bpr);
+  a.x_row_stride = l.x_row_stride / 16;
+  a.scale_row_stride = l.scale_row_stride;
+  a.out_row_stride = l.out_row_stride / 16;
   a.x_share_stride = l.x_share_stride / 16;
   a.scale_share_stride = l.scale_share_stride;
-  const uint64_t per_block = static_cast<uint64_t>(QRS_BLOCK) * QRS_CHUNKS_PER_LANE;
-  const uint64_t blocks = (a.n_chunks + per_block - 1) / per_block;
-  if (blocks == 0 || blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  if (l.n_shares != 1 && l.n_shares != W) return hipErrorInvalidValue;
-  if (l.x_share_stride % 16) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF>), dim3(static_cast<uint32_t>(blocks), l.n_shares), dim3(QRS_BLOCK),
-                     0, stream, a);
+  const dim3 grid(static_cast<uint32_t>(blocks), l.n_shares);
+  if (l.n_shares > 1) {
+    if (l.n_rows != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF, kAddrShares>), grid, dim3(QRS_BLOCK), 0, stream, a);
+  } else if (l.n_rows > 1) {
+    hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF, kAddrRows>), grid, dim3(QRS_BLOCK), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF, kAddrFlat>), grid, dim3(QRS_BLOCK), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
 template <int W, int XF, int SL>
 hipError_t dispatch_out(const ReduceLaunch& l, hipStream_t s) {
-  return l.out_format == kOutF32 ? launch_typed<W, XF, SL, kOutF32>(l, s) : launch_typed<W, XF, SL, kOutBF16>(l, s);
+  switch (l.out_format) {
+    case kOutF32: return launch_typed<W, XF, SL, kOutF32>(l, s);
+    case kOutBF16: return launch_typed<W, XF, SL, kOutBF16>(l, s);
+    case kOutF16: return launch_typed<W, XF, SL, kOutF16>(l, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int W>

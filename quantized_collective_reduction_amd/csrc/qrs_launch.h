@@ -13,12 +13,15 @@ constexpr int kMaxWorld = 8;
 // Element and scale formats as the kernels see them.
 enum XFormat : int { kXInt8 = 0, kXE4M3FN = 1, kXE5M2 = 2 };
 enum ScaleLayout : int { kScaleF32Group128 = 0, kScaleE8M0Block32 = 1 };
-enum OutFormat : int { kOutF32 = 0, kOutBF16 = 1 };
+enum OutFormat : int { kOutF32 = 0, kOutBF16 = 1, kOutF16 = 2 };
 
-// One launch of the dequant + rank-ordered reduce over a flat [rows*H]
-// element range per share. Every slice is contiguous row-major, so element e
-// of a share lives at offset e in every x slice and in the output, and its
-// scale at offset e / G in every scale slice (G divides H).
+// One launch of the dequant + rank-ordered reduce. A share is n_rows rows of
+// row_elems elements (a multiple of 128). Element c of row i of rank r's
+// slice is byte i * x_row_stride + c of x[r]; its scale is element c / G of
+// the row that starts i * scale_row_stride bytes into scales[r]; the output
+// row starts i * out_row_stride bytes into the output. A contiguous share is
+// the case n_rows = 1, row_elems = rows * H (G divides H, so the flat
+// indexing is the same), strides unused.
 //
 // n_shares == 1: x[r] / scales[r] point at rank r's slice of this GPU's
 // share, out[0] at the share's output.
@@ -31,8 +34,12 @@ struct ReduceLaunch {
   XFormat x_format;
   ScaleLayout scale_layout;
   OutFormat out_format;
-  uint64_t n_elems;        // rows * H per share, a multiple of 128
-  int n_shares;            // 1 or world_size
+  uint64_t n_rows;
+  uint64_t row_elems;
+  uint64_t x_row_stride;      // bytes, a multiple of 16
+  uint64_t scale_row_stride;  // bytes
+  uint64_t out_row_stride;    // bytes, a multiple of 16
+  int n_shares;               // 1 or world_size
   uint64_t x_share_stride;      // bytes between consecutive shares' x row blocks
   uint64_t scale_share_stride;  // bytes between consecutive shares' scale row blocks
   const void* x[kMaxWorld];

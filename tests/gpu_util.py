@@ -19,9 +19,11 @@ def to_device(xs, ss, dev="cuda"):
     return dx, ds
 
 
+OUT_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
 def empty_out(rows, h, out_dtype, dev="cuda"):
-    dt = torch.float32 if out_dtype == "f32" else torch.bfloat16
-    return torch.empty((rows, h), dtype=dt, device=dev)
+    return torch.empty((rows, h), dtype=OUT_TORCH[out_dtype], device=dev)
 
 
 def out_bits(out_t):
@@ -48,9 +50,9 @@ def oracle_bits(oracle_out, out_dtype):
 
 
 def assert_parity(got_bits, want_bits, out_dtype, what=""):
-    """fp32: bit-exact (any NaN equals any NaN). bf16: within 1 ulp in the
-    ordered-integer sense, NaN equals NaN; returns the count of elements that
-    are not bit-identical."""
+    """fp32: bit-exact (any NaN equals any NaN). bf16 / fp16: within 1 ulp in
+    the ordered-integer sense, NaN equals NaN; returns the count of elements
+    that are not bit-identical."""
     assert got_bits.shape == want_bits.shape, what
     if out_dtype == "f32":
         g_nan = (got_bits & 0x7FFFFFFF) > 0x7F800000
@@ -60,8 +62,9 @@ def assert_parity(got_bits, want_bits, out_dtype, what=""):
         bad = np.nonzero(got_bits[ok] != want_bits[ok])[0]
         assert bad.size == 0, f"{what}: {bad.size} fp32 mismatches, first at flat {np.nonzero(ok)[0][bad[0]]}"
         return 0
-    g_nan = (got_bits & 0x7FFF) > 0x7F80
-    w_nan = (want_bits & 0x7FFF) > 0x7F80
+    inf_bits = 0x7F80 if out_dtype == "bf16" else 0x7C00
+    g_nan = (got_bits & 0x7FFF) > inf_bits
+    w_nan = (want_bits & 0x7FFF) > inf_bits
     assert np.array_equal(g_nan, w_nan), f"{what}: NaN positions differ"
     ok = ~w_nan
 
@@ -70,5 +73,5 @@ def assert_parity(got_bits, want_bits, out_dtype, what=""):
         return np.where(b & 0x8000, 0x8000 - b, b)  # sign-magnitude -> ordered (+0 == -0)
 
     d = np.abs(ordered(got_bits[ok]) - ordered(want_bits[ok]))
-    assert d.size == 0 or d.max() <= 1, f"{what}: bf16 distance {d.max()} ulp"
+    assert d.size == 0 or d.max() <= 1, f"{what}: {out_dtype} distance {d.max()} ulp"
     return int(np.count_nonzero(d))

@@ -47,7 +47,7 @@ VALID_MODES = [
 
 
 @pytest.mark.parametrize("x,s", VALID_MODES)
-@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("out", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("w", [2, 4, 8])
 def test_valid_plans(lib, x, s, out, w):
     p = qrs.plan(w, 16 * w, 1024, x, s, out)
@@ -168,3 +168,23 @@ def test_prepared_launch_checks_arguments_on_host(lib):
         qrs.Launch(p, x, s, out)  # CPU tensors
     with pytest.raises(ValueError):
         qrs.Launch(p, x, s, torch.zeros(16, 1024, dtype=torch.float32))  # wrong output size
+
+
+def test_strided_run_rejects_bad_strides_on_host(lib):
+    p = qrs.plan(2, 32, 1024, "e4m3fn", "e8m0_block32", "f32")
+    A = 1 << 40
+    xs = (ctypes.c_void_p * 2)(A, A + (1 << 30))
+    ss = (ctypes.c_void_p * 2)(A + (2 << 30), A + (3 << 30))
+    out = A + (4 << 30)
+
+    def call(ldx, lds, ldo, o=out):
+        return lib.qrs_run_strided(p.handle, xs, ldx, ss, lds, o, ldo, None, 0, None)
+
+    assert call(1000, 32, 1024) == qrs.Status.INVALID_ARG  # x stride < h
+    assert call(1032, 32, 1024) == qrs.Status.INVALID_ARG  # not a multiple of 16
+    assert call(1024, 31, 1024) == qrs.Status.INVALID_ARG  # scale stride < h/32
+    assert call(1024, 32, 1020) == qrs.Status.INVALID_ARG  # out stride < h
+    assert call(1024, 32, 1026) == qrs.Status.INVALID_ARG  # 1026 * 4 bytes is not a multiple of 16
+    assert call(1024, 32, 1024, o=out + 4) == qrs.Status.INVALID_ARG  # misaligned out
+    # out span overlapping the last row of rank 1's x slice
+    assert call(4096, 32, 1024, o=A + (1 << 30) + 15 * 4096) == qrs.Status.INVALID_ARG

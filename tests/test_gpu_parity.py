@@ -48,7 +48,7 @@ def test_workload_full_size(gpu, name):
 
 
 @pytest.mark.parametrize("x_format,scale_layout", MODES)
-@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("w", [2, 4, 8])
 @pytest.mark.parametrize("h", [1024, 1152, 5120, 8192])
 def test_sweep_small_ragged(gpu, x_format, scale_layout, out_dtype, w, h):
@@ -82,7 +82,7 @@ def test_non_finite_and_extreme_codes(gpu):
     fp32 scales with zeros, negatives, subnormals and huge values."""
     rng = np.random.default_rng(99)
     for x_format, scale_layout in MODES:
-        for out_dtype in ("f32", "bf16"):
+        for out_dtype in ("f32", "bf16", "f16"):
             w, rows, h = 4, 16, 1024
             g = 128 if scale_layout == "f32_group128" else 32
             xs = [rng.integers(0, 256, size=(rows, h), dtype=np.uint8) for _ in range(w)]

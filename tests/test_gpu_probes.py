@@ -27,7 +27,7 @@ ONE_CODE = {"int8": 0x01, "e4m3fn": 0x38, "e5m2": 0x3C}
     [("int8", "f32_group128"), ("e4m3fn", "f32_group128"), ("e5m2", "f32_group128"),
      ("e4m3fn", "e8m0_block32"), ("e5m2", "e8m0_block32")],
 )
-@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
 def test_every_x_code_decodes_exactly(gpu, x_format, scale_layout, out_dtype):
     rows, h = 2, 1024
     codes = np.tile(np.arange(256, dtype=np.uint8), rows * h // 256).reshape(rows, h)

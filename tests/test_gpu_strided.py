@@ -1,0 +1,81 @@
+"""GPU parity of qrs_run_strided: slices and outputs that are row ranges of
+wider buffers (column windows of [rows, H_total] tensors)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_collective_reduction_amd as qrs
+import workloads
+from gpu_util import OUT_TORCH, assert_parity, oracle_bits, out_bits
+
+pytestmark = pytest.mark.gpu
+
+MODES = [
+    ("int8", "f32_group128"),
+    ("e4m3fn", "f32_group128"),
+    ("e5m2", "f32_group128"),
+    ("e4m3fn", "e8m0_block32"),
+    ("e5m2", "e8m0_block32"),
+]
+
+
+def _case(w, rows, h, x_format, scale_layout, out_dtype, extra_cols, c0, seed):
+    g = 128 if scale_layout == "f32_group128" else 32
+    ht = h + extra_cols
+    wl = workloads.Workload("strided", w, rows * w, ht, x_format, scale_layout, out_dtype,
+                            x_dist="int_uniform" if x_format == "int8" else "normal",
+                            x_param=127 if x_format == "int8" else 30,
+                            scale_lo=-10 if scale_layout == "f32_group128" else 110,
+                            scale_hi=2 if scale_layout == "f32_group128" else 140, seed=seed)
+    xs_full, ss_full = workloads.generate(wl)  # [rows, ht] per rank
+    xs = [x[:, c0:c0 + h] for x in xs_full]
+    ss = [s[:, c0 // g:(c0 + h) // g] for s in ss_full]
+    want = oracle.reduce_scatter_share([np.ascontiguousarray(x) for x in xs], [np.ascontiguousarray(s) for s in ss],
+                                       x_format, scale_layout, out_dtype)
+    dx_full = [torch.from_numpy(x).cuda() for x in xs_full]
+    ds_full = [torch.from_numpy(s).cuda() for s in ss_full]
+    dx = [t[:, c0:c0 + h] for t in dx_full]
+    ds = [t[:, c0 // g:(c0 + h) // g] for t in ds_full]
+    oc0 = 64
+    out_full = torch.full((rows, h + 192), float("nan"), dtype=OUT_TORCH[out_dtype], device="cuda")
+    out = out_full[:, oc0:oc0 + h]
+    p = qrs.plan(w, rows * w, h, x_format, scale_layout, out_dtype)
+    qrs.run_strided(p, dx, ds, out)
+    torch.cuda.synchronize()
+    got = out_bits(out.contiguous())
+    assert_parity(got, oracle_bits(want, out_dtype), out_dtype, f"W={w} H={h} {x_format}/{scale_layout}->{out_dtype}")
+    # Nothing outside the window was written.
+    full_bits = out_bits(out_full)
+    pad = np.concatenate([full_bits[:, :oc0], full_bits[:, oc0 + h:]], axis=1)
+    sentinel = out_bits(torch.full((1, 1), float("nan"), dtype=OUT_TORCH[out_dtype]))[0, 0]
+    assert np.all(pad == sentinel)
+    # Same bits as qrs_run on contiguous copies.
+    out2 = torch.empty((rows, h), dtype=OUT_TORCH[out_dtype], device="cuda")
+    qrs.run(p, [t.contiguous() for t in dx], [t.contiguous() for t in ds], out2)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_bits(out2), got)
+
+
+@pytest.mark.parametrize("x_format,scale_layout", MODES)
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("w", [2, 8])
+def test_column_window(gpu, x_format, scale_layout, out_dtype, w):
+    _case(w, 7, 1152, x_format, scale_layout, out_dtype, extra_cols=384, c0=128, seed=w)
+
+
+@pytest.mark.parametrize("h", [1024, 5120, 8192])
+def test_wide_rows_and_equal_stride(gpu, h):
+    _case(4, 5, h, "e4m3fn", "e8m0_block32", "f32", extra_cols=256, c0=256, seed=h)
+    _case(4, 3, h, "e5m2", "f32_group128", "bf16", extra_cols=0, c0=0, seed=h + 1)  # stride == H
+
+
+def test_strided_rejects_mismatched_strides(gpu):
+    p = qrs.plan(2, 8, 1024, "e4m3fn", "e8m0_block32", "f32")
+    a = torch.zeros(4, 2048, dtype=torch.uint8, device="cuda")
+    b = torch.zeros(4, 1024 + 512, dtype=torch.uint8, device="cuda")
+    s = [torch.zeros(4, 32, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    out = torch.zeros(4, 1024, dtype=torch.float32, device="cuda")
+    with pytest.raises(ValueError):
+        qrs.run_strided(p, [a[:, :1024], b[:, :1024]], s, out)

@@ -191,7 +191,7 @@ def test_non_finite_propagation():
     assert math.isnan(f([x(0x00), x(0x00)], [nan_scale, one], "e5m2"))
 
 
-def test_bf16_output_is_rounded_fp32_output():
+def test_16bit_outputs_are_rounded_fp32_output():
     wl = workloads.CONFIGS["C2"].with_(bs=4 * 8)
     xs, ss = workloads.generate(wl)
     f = reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, "f32")
@@ -199,6 +199,8 @@ def test_bf16_output_is_rounded_fp32_output():
     tb = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(b, fp32_to_bf16_bits(f))
     assert np.array_equal(b, tb)
+    h = reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, "f16")
+    assert np.array_equal(h, f.astype(np.float16).view(np.uint16))
 
 
 # ------------------------------------------------------------ error bound

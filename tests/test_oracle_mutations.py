@@ -9,13 +9,13 @@ import torch
 
 import workloads
 from oracle.decode import GROUP_SIZE, decode_table, scale_decode_table
-from oracle.reduce import fp32_to_bf16_bits, reduce_scatter_share
+from oracle.reduce import fp32_to_bf16_bits, fp32_to_f16_bits, reduce_scatter_share
 
 from test_oracle_closed_forms import build_example, load_worked_examples
 
 
 def _fold(xs, ss, xf, sl, out, *, order=None, start_zero=False, wide=False, pairwise=False, group=None,
-          to_bf16=fp32_to_bf16_bits):
+          to_bf16=fp32_to_bf16_bits, to_f16=fp32_to_f16_bits):
     """A configurable re-statement of the definition used only to plant mistakes."""
     g = group or GROUP_SIZE[sl]
     xt = decode_table(xf)
@@ -42,11 +42,22 @@ def _fold(xs, ss, xf, sl, out, *, order=None, start_zero=False, wide=False, pair
         for p in (ps if start_zero else ps[1:]):
             acc = acc + p
     acc = acc.astype(np.float32)
-    return acc if out == "f32" else to_bf16(acc)
+    if out == "f32":
+        return acc
+    return to_f16(acc) if out == "f16" else to_bf16(acc)
 
 
 def _truncate_bf16(acc):
     return (np.ascontiguousarray(acc).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _f16_toward_zero(acc):
+    """binary16 by truncation toward zero (a plausible wrong rounding)."""
+    a = np.ascontiguousarray(acc, dtype=np.float32).astype(np.float64)
+    _, e2 = np.frexp(np.abs(a))
+    q = np.ldexp(1.0, np.maximum(e2 - 1, -14) - 10)
+    r = np.minimum(np.trunc(np.abs(a) / q) * q, 65504.0)
+    return (np.copysign(r, a).astype(np.float16)).view(np.uint16)
 
 
 def _worked_examples_pass(fn):
@@ -85,6 +96,7 @@ MUTANTS = {
     "fp64_accumulate_like_fma": dict(wide=True),
     "accumulator_starts_at_plus_zero": dict(start_zero=True),
     "bf16_by_truncation": dict(to_bf16=_truncate_bf16),
+    "f16_toward_zero": dict(to_f16=_f16_toward_zero),
     "group_of_64_columns": dict(group=64),
 }
 

@@ -38,7 +38,7 @@ class Workload:
     h: int
     x_format: str  # "int8" | "e4m3fn" | "e5m2"
     scale_layout: str  # "f32_group128" | "e8m0_block32"
-    out_dtype: str  # "f32" | "bf16"
+    out_dtype: str  # "f32" | "bf16" | "f16"
     # x values: "int_uniform" draws integers in [-x_param, x_param];
     # "normal" draws N(0,1) * x_param, clipped to the format's finite range.
     x_dist: str = "normal"
