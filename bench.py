@@ -5,9 +5,10 @@ reduce-scatter (dequant + rank-ordered reduce) on MI355X.
 
 A step is one launch of the whole hot path (decode, scale, rank-ordered fp32
 fold, convert, store) over one batch: W rank slices of the workload, already
-resident in HBM. Several identical input/output sets are allocated and the
-steps rotate through them, so the working set of consecutive steps (well over
-the 256 MB Infinity Cache) is not served from that cache.
+resident in HBM, placed in one buffer at the pitch qrs_slice_pitch recommends
+(--layout). Several identical input/output sets are allocated and the steps
+rotate through them, so the working set of consecutive steps (well over the
+256 MB Infinity Cache) is not served from that cache.
 
 Prints ONE JSON line on stdout:
   value            whole-job throughput: algorithmic bytes x K / wall time of
@@ -31,6 +32,8 @@ import os
 import statistics
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -101,29 +104,47 @@ def cpu_baseline(wl, xs, ss, min_seconds=10.0, min_reps=3):
     }
 
 
-def setup_share(wl, dev, qrs, workloads, torch):
+def place_inputs(p, xs, ss, dev, qrs, torch, layout, full_inputs=False):
+    """Device copies of the W rank inputs in the requested placement:
+    "pitched" - one x buffer and one scale buffer, slices at the pitch
+                qrs_slice_pitch recommends (the default);
+    "packed"  - one [W, rows, H] x buffer and one scale buffer, slices back
+                to back;
+    "separate" - one allocation per slice."""
+    if layout == "pitched":
+        dx, ds = qrs.alloc_slices(p, device=dev, full_inputs=full_inputs)
+        for t, a in zip(dx, xs):
+            t.copy_(torch.from_numpy(a))
+        for t, a in zip(ds, ss):
+            t.copy_(torch.from_numpy(a))
+        return dx, ds
+    if layout == "packed":
+        bx = torch.from_numpy(np.stack(xs)).to(dev)
+        bs_ = torch.from_numpy(np.stack(ss)).to(dev)
+        return [bx[r] for r in range(len(xs))], [bs_[r] for r in range(len(ss))]
+    return [torch.from_numpy(a).to(dev) for a in xs], [torch.from_numpy(a).to(dev) for a in ss]
+
+
+def setup_share(wl, dev, qrs, workloads, torch, layout):
     """This GPU's share (qrs_run): W slices [rows, H] -> [rows, H]."""
     alg_bytes = wl.algorithmic_bytes()
     t0 = time.perf_counter()
     xs, ss = workloads.generate(wl)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
     n_sets = max(2, -(-4 * MALL_BYTES // alg_bytes))
-    out_dt = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
-    dx0 = [torch.from_numpy(x).to(dev) for x in xs]
-    ds0 = [torch.from_numpy(s).to(dev) for s in ss]
+    out_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.out_dtype]
     p = qrs.plan(wl.world_size, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
     stream = torch.cuda.current_stream(dev)
     launches, outs = [], []
-    for k in range(n_sets):
-        dx = dx0 if k == 0 else [t.clone() for t in dx0]
-        ds = ds0 if k == 0 else [t.clone() for t in ds0]
+    for _ in range(n_sets):
+        dx, ds = place_inputs(p, xs, ss, dev, qrs, torch, layout)
         out = torch.empty((wl.rows, wl.h), dtype=out_dt, device=dev)
         launches.append(qrs.Launch(p, dx, ds, out, stream=stream))
         outs.append([out])
     return alg_bytes, launches, outs, (xs, ss)
 
 
-def setup_all_shares(wl, dev, qrs, workloads, torch):
+def setup_all_shares(wl, dev, qrs, workloads, torch, layout):
     """The group's whole reduce-scatter on this GPU (qrs_run_all_shares):
     W inputs [BS, H] -> W shares [BS/W, H], the all-to-all by addressing."""
     alg_bytes = wl.world_size * wl.algorithmic_bytes()
@@ -131,22 +152,19 @@ def setup_all_shares(wl, dev, qrs, workloads, torch):
     xs, ss = workloads.generate_full(wl)
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
     n_sets = max(2, -(-4 * MALL_BYTES // alg_bytes))
-    out_dt = torch.float32 if wl.out_dtype == "f32" else torch.bfloat16
-    dx0 = [torch.from_numpy(x).to(dev) for x in xs]
-    ds0 = [torch.from_numpy(s).to(dev) for s in ss]
+    out_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.out_dtype]
     p = qrs.plan(wl.world_size, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
     stream = torch.cuda.current_stream(dev)
     launches, outs = [], []
-    for k in range(n_sets):
-        dx = dx0 if k == 0 else [t.clone() for t in dx0]
-        ds = ds0 if k == 0 else [t.clone() for t in ds0]
+    for _ in range(n_sets):
+        dx, ds = place_inputs(p, xs, ss, dev, qrs, torch, layout, full_inputs=True)
         o = [torch.empty((wl.rows, wl.h), dtype=out_dt, device=dev) for _ in range(wl.world_size)]
         launches.append(qrs.AllSharesLaunch(p, dx, ds, o, stream=stream))
         outs.append(o)
     return alg_bytes, launches, outs, None
 
 
-def setup_quantize(wl, dev, qrs, workloads, torch):
+def setup_quantize(wl, dev, qrs, workloads, torch, layout):
     """Producer-side quantization (qrs_quantize) of one rank's bf16
     activations [BS, H] into the workload's x format and scale layout."""
     n = wl.bs * wl.h
@@ -183,6 +201,9 @@ def main():
                     help="share: this GPU's share (the hot path, default); all_shares: every rank's share "
                          "from the inputs before the all-to-all, in one launch; quantize: the producer-side "
                          "quantization of one rank's bf16 activations [BS, H]")
+    ap.add_argument("--layout", default="pitched", choices=["pitched", "packed", "separate"],
+                    help="placement of the W rank slices: pitched (one buffer, the pitch qrs_slice_pitch "
+                         "recommends; default), packed (one buffer, back to back), separate (one allocation each)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (cpu_baseline = null)")
     args = ap.parse_args()
 
@@ -207,7 +228,7 @@ def main():
     wl = workloads.CONFIGS[args.workload]
     log(f"[bench] {args.op} on {wl.name}: W={wl.world_size} BS={wl.bs} H={wl.h} rows={wl.rows} "
         f"{wl.x_format}/{wl.scale_layout}->{wl.out_dtype}")
-    alg_bytes, launches, outs, host_inputs = OPS[args.op](wl, dev, qrs, workloads, torch)
+    alg_bytes, launches, outs, host_inputs = OPS[args.op](wl, dev, qrs, workloads, torch, args.layout)
     n_sets = len(launches)
     stream = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
@@ -284,6 +305,7 @@ def main():
                         + {"share": "", "all_shares": ", all W shares from the pre-all-to-all inputs",
                            "quantize": f", quantize one rank's bf16 [{wl.bs}, {wl.h}]"}[args.op],
             "op": args.op,
+            "layout": args.layout if args.op != "quantize" else None,
             "world_size": wl.world_size,
             "bs": wl.bs,
             "rows": wl.rows,

@@ -229,6 +229,27 @@ qrs_status qrs_plan_destroy(qrs_plan_t plan);
  * may be NULL. */
 qrs_status qrs_plan_shape(qrs_plan_t plan, int64_t* rows_out, int64_t* h_out);
 
+/*
+ * Recommended placement when the W rank slices of x (and of the scales)
+ * share one allocation, for example the receive buffer of the all-to-all:
+ * slice r at byte offset r * x_pitch (scales: r * scale_pitch). Slices
+ * placed exactly rows*H bytes apart put the same offset of every slice in
+ * the same HBM bank group, and the W concurrent read streams then evict each
+ * other's DRAM rows; staggering consecutive slices by a bit over 1 MiB
+ * avoids it (measured on MI355X with 16 MiB slices: 31.5 us back to back,
+ * 28.9 us staggered). Any placement gives the same results; this only
+ * affects speed. Offsets are multiples of 64 KiB (x) and 4 KiB (scales), so
+ * alignment requirements hold.
+ *
+ *   x_pitch_out, scale_pitch_out  receive the pitches in bytes; either may be
+ *                                 NULL.
+ *   full_inputs                   0: pitches for this GPU's slices ([rows, H]
+ *                                 each, for qrs_run); 1: for the ranks' whole
+ *                                 inputs ([BS, H] each, for
+ *                                 qrs_run_all_shares).
+ */
+qrs_status qrs_slice_pitch(qrs_plan_t plan, int full_inputs, size_t* x_pitch_out, size_t* scale_pitch_out);
+
 /* Static, never-null name of a status code. */
 const char* qrs_status_string(qrs_status status);
 

@@ -32,6 +32,8 @@ __all__ = [
     "run",
     "run_all_shares",
     "run_strided",
+    "slice_pitch",
+    "alloc_slices",
     "quantize",
     "Launch",
     "AllSharesLaunch",
@@ -79,6 +81,7 @@ EXPORTED_SYMBOLS = (
     "qrs_quantize",
     "qrs_plan_destroy",
     "qrs_plan_shape",
+    "qrs_slice_pitch",
     "qrs_status_string",
     "qrs_last_error",
     "qrs_stream_copy",
@@ -120,6 +123,8 @@ def load_library(path: str = LIB_PATH):
     lib.qrs_plan_destroy.restype = c_int
     lib.qrs_plan_shape.argtypes = [vp, ctypes.POINTER(c_i64), ctypes.POINTER(c_i64)]
     lib.qrs_plan_shape.restype = c_int
+    lib.qrs_slice_pitch.argtypes = [vp, c_int, ctypes.POINTER(c_sz), ctypes.POINTER(c_sz)]
+    lib.qrs_slice_pitch.restype = c_int
     lib.qrs_status_string.argtypes = [c_int]
     lib.qrs_status_string.restype = ctypes.c_char_p
     lib.qrs_last_error.argtypes = []
@@ -180,6 +185,37 @@ class Plan:
 
 def plan(world_size, bs, h, x_dtype, scale_layout, out_dtype) -> Plan:
     return Plan(world_size, bs, h, x_dtype, scale_layout, out_dtype)
+
+
+def slice_pitch(p: Plan, full_inputs=False):
+    """Recommended byte distance between consecutive rank slices of x and of
+    the scales when each kind shares one allocation (qrs_slice_pitch)."""
+    lib = load_library()
+    xp, sp = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib.qrs_slice_pitch(p.handle, 1 if full_inputs else 0, ctypes.byref(xp), ctypes.byref(sp)))
+    return xp.value, sp.value
+
+
+def alloc_slices(p: Plan, device="cuda", full_inputs=False):
+    """One x buffer and one scale buffer holding the W rank slices at the
+    recommended pitch. Returns (x_views, scale_views): lists of W contiguous
+    device views, ``[rows, H]`` uint8 and ``[rows, H/G]`` fp32 or uint8
+    (``rows`` = BS with ``full_inputs``)."""
+    import torch
+
+    w = p.world_size
+    rows = p.bs if full_inputs else p.rows
+    xp, sp = slice_pitch(p, full_inputs)
+    g = p.group
+    x_buf = torch.empty(xp * w, dtype=torch.uint8, device=device)
+    s_buf = torch.empty(sp * w, dtype=torch.uint8, device=device)
+    xs = [x_buf[r * xp:r * xp + rows * p.h].view(rows, p.h) for r in range(w)]
+    n_s = rows * p.h // g
+    if p.scale_layout == ScaleLayout.F32_GROUP128:
+        ss = [s_buf[r * sp:r * sp + 4 * n_s].view(torch.float32).view(rows, p.h // g) for r in range(w)]
+    else:
+        ss = [s_buf[r * sp:r * sp + n_s].view(rows, p.h // g) for r in range(w)]
+    return xs, ss
 
 
 def _ptr(t):

@@ -133,6 +133,20 @@ qrs_status qrs_plan_shape(qrs_plan_t plan, int64_t* rows_out, int64_t* h_out) {
   return ok();
 }
 
+qrs_status qrs_slice_pitch(qrs_plan_t plan, int full_inputs, size_t* x_pitch_out, size_t* scale_pitch_out) {
+  if (!plan) return fail(QRS_ERR_INVALID_ARG, "null plan");
+  if (full_inputs != 0 && full_inputs != 1) return fail(QRS_ERR_INVALID_ARG, "full_inputs must be 0 or 1");
+  const uint64_t rows = static_cast<uint64_t>(full_inputs ? plan->bs : plan->rows);
+  const uint64_t x_bytes = rows * static_cast<uint64_t>(plan->h);
+  const uint64_t s_bytes = plan->scale_layout == qrs::kScaleF32Group128 ? x_bytes / 128 * 4 : x_bytes / 32;
+  // Round up to the alignment unit, then add a stagger of 1.25 MiB (x) and
+  // 40 KiB (scales, 1/32 of the x stagger).
+  auto round_up = [](uint64_t v, uint64_t a) { return (v + a - 1) / a * a; };
+  if (x_pitch_out) *x_pitch_out = round_up(x_bytes, 64 * 1024) + 1280 * 1024;
+  if (scale_pitch_out) *scale_pitch_out = round_up(s_bytes, 4096) + 40 * 1024;
+  return ok();
+}
+
 qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* const* scale_slices, void* out,
                    void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;

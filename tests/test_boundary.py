@@ -188,3 +188,16 @@ def test_strided_run_rejects_bad_strides_on_host(lib):
     assert call(1024, 32, 1024, o=out + 4) == qrs.Status.INVALID_ARG  # misaligned out
     # out span overlapping the last row of rank 1's x slice
     assert call(4096, 32, 1024, o=A + (1 << 30) + 15 * 4096) == qrs.Status.INVALID_ARG
+
+
+def test_slice_pitch(lib):
+    p = qrs.plan(8, 16384, 8192, "e4m3fn", "e8m0_block32", "bf16")
+    xp, sp = qrs.slice_pitch(p)
+    assert xp == 16 * 2**20 + 1280 * 1024 and sp == 2048 * 8192 // 32 + 40 * 1024
+    xp, sp = qrs.slice_pitch(p, full_inputs=True)
+    assert xp == 16384 * 8192 + 1280 * 1024
+    p2 = qrs.plan(2, 6, 1152, "int8", "f32_group128", "f32")  # 3 rows: 3456 bytes per slice
+    xp, sp = qrs.slice_pitch(p2)
+    assert xp == 65536 + 1280 * 1024 and xp % 65536 == 0 and sp == 4096 + 40 * 1024
+    assert lib.qrs_slice_pitch(None, 0, None, None) == qrs.Status.INVALID_ARG
+    assert lib.qrs_slice_pitch(p.handle, 2, None, None) == qrs.Status.INVALID_ARG

@@ -192,3 +192,34 @@ def test_prepared_launch_matches_run(gpu):
     assert np.array_equal(out_bits(o1), out_bits(o2))
     want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype), wl.out_dtype)
     assert_parity(out_bits(o2), want, wl.out_dtype, "Launch")
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_recommended_slice_placement(gpu, full):
+    """Slices placed by qrs.alloc_slices (one buffer, recommended pitch) give
+    the oracle's bits, for this GPU's share and for all shares."""
+    import quantized_collective_reduction_amd as qrs
+
+    wl = workloads.CONFIGS["C4"].with_(bs=8 * 12, h=2048)
+    p = qrs.plan(8, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    xs, ss = workloads.generate_full(wl) if full else workloads.generate(wl)
+    dx, ds = qrs.alloc_slices(p, full_inputs=full)
+    for t, a in zip(dx, xs):
+        t.copy_(torch.from_numpy(a))
+    for t, a in zip(ds, ss):
+        t.copy_(torch.from_numpy(a))
+    xp, sp = qrs.slice_pitch(p, full_inputs=full)
+    assert dx[1].data_ptr() - dx[0].data_ptr() == xp and ds[1].data_ptr() - ds[0].data_ptr() == sp
+    if full:
+        outs = [empty_out(wl.rows, wl.h, wl.out_dtype) for _ in range(8)]
+        qrs.run_all_shares(p, dx, ds, outs)
+        torch.cuda.synchronize()
+        want = oracle.all_shares(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype)
+        for j in range(8):
+            assert_parity(out_bits(outs[j]), oracle_bits(want[j], wl.out_dtype), wl.out_dtype, f"share {j}")
+    else:
+        out = empty_out(wl.rows, wl.h, wl.out_dtype)
+        qrs.run(p, dx, ds, out)
+        torch.cuda.synchronize()
+        want = oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype)
+        assert_parity(out_bits(out), oracle_bits(want, wl.out_dtype), wl.out_dtype, "pitched")
