@@ -201,3 +201,50 @@ def test_slice_pitch(lib):
     assert xp == 65536 + 1280 * 1024 and xp % 65536 == 0 and sp == 4096 + 40 * 1024
     assert lib.qrs_slice_pitch(None, 0, None, None) == qrs.Status.INVALID_ARG
     assert lib.qrs_slice_pitch(p.handle, 2, None, None) == qrs.Status.INVALID_ARG
+
+
+def test_quantize_rejects_bad_arguments_on_host(lib):
+    A = 1 << 40
+    x, c, s = A, A + (1 << 30), A + (2 << 30)
+
+    def q(tokens=16, h=1024, xd=1, sl=1, xp=x, cp=c, sp=s):
+        return lib.qrs_quantize(tokens, h, xd, sl, xp, cp, sp, None)
+
+    assert q(tokens=0) == qrs.Status.INVALID_ARG
+    assert q(tokens=-3) == qrs.Status.INVALID_ARG
+    assert q(h=1000) == qrs.Status.INVALID_ARG
+    assert q(h=9216) == qrs.Status.INVALID_ARG
+    assert q(xd=3) == qrs.Status.UNSUPPORTED  # HIFLOAT8
+    assert q(xd=0, sl=1) == qrs.Status.INVALID_ARG  # INT8 with E8M0
+    assert q(xd=9) == qrs.Status.INVALID_ARG
+    assert q(sl=4) == qrs.Status.INVALID_ARG
+    assert q(xp=0) == qrs.Status.INVALID_ARG
+    assert q(xp=x + 8) == qrs.Status.INVALID_ARG  # input misaligned
+    assert q(cp=c + 8) == qrs.Status.INVALID_ARG  # codes misaligned
+    assert q(sl=0, xd=1, sp=s + 2) == qrs.Status.INVALID_ARG  # fp32 scales misaligned
+    assert q(cp=x + 1024) == qrs.Status.INVALID_ARG  # codes overlap the input
+    assert q(sp=c + 100) == qrs.Status.INVALID_ARG  # scales overlap the codes
+    assert b"overlap" in lib.qrs_last_error()
+
+
+def test_all_shares_rejects_bad_arguments_on_host(lib):
+    p = qrs.plan(2, 32, 1024, "e4m3fn", "f32_group128", "bf16")
+    A = 1 << 40
+    G = 1 << 30
+    xs = (ctypes.c_void_p * 2)(A, A + G)
+    ss = (ctypes.c_void_p * 2)(A + 2 * G, A + 3 * G)
+
+    def run(o0, o1, x=xs, s=ss):
+        outs = (ctypes.c_void_p * 2)(o0, o1)
+        return lib.qrs_run_all_shares(p.handle, x, s, outs, None, 0, None)
+
+    assert lib.qrs_run_all_shares(None, xs, ss, (ctypes.c_void_p * 2)(A + 4 * G, A + 5 * G), None, 0, None) \
+        == qrs.Status.INVALID_ARG
+    assert run(A + 4 * G, 0) == qrs.Status.INVALID_ARG  # null output
+    assert run(A + 4 * G, A + 4 * G + 16) == qrs.Status.INVALID_ARG  # outputs overlap
+    assert run(A + 4 * G + 4, A + 5 * G) == qrs.Status.INVALID_ARG  # misaligned output
+    assert run(A + 32 * 1024 - 16, A + 5 * G) == qrs.Status.INVALID_ARG  # output overlaps rank 0's x
+    bad_x = (ctypes.c_void_p * 2)(A + 8, A + G)
+    assert run(A + 4 * G, A + 5 * G, x=bad_x) == qrs.Status.INVALID_ARG  # misaligned x
+    bad_s = (ctypes.c_void_p * 2)(A + 2 * G + 2, A + 3 * G)
+    assert run(A + 4 * G, A + 5 * G, s=bad_s) == qrs.Status.INVALID_ARG  # misaligned fp32 scales

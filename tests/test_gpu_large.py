@@ -1,0 +1,41 @@
+"""Largest shapes: an fp32 output past 4 GiB (byte offsets beyond 2^32) from
+1 GiB input slices, checked against the oracle on a repeating row block."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_collective_reduction_amd as qrs
+import workloads
+from gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("x_format,scale_layout", [("e5m2", "e8m0_block32"), ("int8", "f32_group128")])
+def test_output_beyond_4gib(gpu, x_format, scale_layout):
+    w, h, rows, blk = 2, 8192, 133120, 64  # output 4.06 GiB: byte offsets past 2^32
+    wl = workloads.Workload("large", w, w * blk, h, x_format, scale_layout, "f32",
+                            x_dist="int_uniform" if x_format == "int8" else "normal",
+                            x_param=127 if x_format == "int8" else 300,
+                            scale_lo=-8 if scale_layout == "f32_group128" else 110,
+                            scale_hi=0 if scale_layout == "f32_group128" else 140, seed=31)
+    xs, ss = workloads.generate(wl)  # one block of 64 rows per rank
+    want = oracle.reduce_scatter_share(xs, ss, x_format, scale_layout, "f32").view(np.int32)
+    log(f"[large] {x_format}/{scale_layout}: {rows} x {h} fp32 output ({rows * h * 4 / 2**30:.2f} GiB)")
+    reps = rows // blk
+    dx = [torch.from_numpy(x).cuda().repeat(reps, 1) for x in xs]
+    ds = [torch.from_numpy(s).cuda().repeat(reps, 1) for s in ss]
+    out = torch.empty((rows, h), dtype=torch.float32, device="cuda")
+    assert out.numel() * 4 > 2**32
+    p = qrs.plan(w, w * rows, h, x_format, scale_layout, "f32")
+    qrs.run(p, dx, ds, out)
+    torch.cuda.synchronize()
+    del dx, ds
+    want_t = torch.from_numpy(want).cuda()
+    got = out.view(torch.int32).view(reps, blk, h)
+    assert torch.equal(got, want_t.unsqueeze(0).expand(reps, blk, h))
+    # The very last rows, on the host as well.
+    tail = out[-blk:].cpu().view(torch.int32).numpy()
+    assert np.array_equal(tail, want)
