@@ -1,7 +1,7 @@
 """Benchmark: achieved HBM bandwidth of one GPU's share of the quantized
 reduce-scatter (dequant + rank-ordered reduce) on MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload C4] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--op OP] [--gpus 1]
 
 A step is one launch of the whole hot path (decode, scale, rank-ordered fp32
 fold, convert, store) over one batch: W rank slices of the workload, already
@@ -48,6 +48,12 @@ KERNEL_SOURCES = {
     "quantize": "quantized_collective_reduction_amd/csrc/qrs_quantize.hip",
 }
 MALL_BYTES = 256 << 20
+
+
+def workloads_names():
+    import workloads
+
+    return workloads.CONFIGS.keys()
 
 
 def log(msg):
@@ -196,7 +202,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="C4", help="C1..C5 (default C4: W=8, H=8192, the metric's workload)")
+    ap.add_argument("--workload", default="w8_bs16384_h8192_mx_e4m3_bf16", choices=sorted(workloads_names()),
+                    help="default: the W=8, BS=16384, H=8192 MX E4M3FN -> bf16 share")
     ap.add_argument("--op", default="share", choices=sorted(OPS),
                     help="share: this GPU's share (the hot path, default); all_shares: every rank's share "
                          "from the inputs before the all-to-all, in one launch; quantize: the producer-side "

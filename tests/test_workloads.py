@@ -57,11 +57,11 @@ def test_value_ranges(name):
 
 def test_algorithmic_bytes_match_the_size_formulas():
     # x: BS*H bytes over all ranks' slices; scales: BS*H/128*4 or BS*H/32*1.
-    c4 = workloads.CONFIGS["C4"]
+    c4 = workloads.CONFIGS["w8_bs16384_h8192_mx_e4m3_bf16"]
     assert c4.algorithmic_bytes() == 16384 * 8192 + 16384 * 8192 // 32 + 2048 * 8192 * 2 == 171_966_464
-    c5 = workloads.CONFIGS["C5"]
+    c5 = workloads.CONFIGS["w8_bs65536_h5120_mx_e5m2_f32"]
     assert c5.algorithmic_bytes() == 65536 * 5120 + 65536 * 5120 // 32 + 8192 * 5120 * 4 == 513_802_240
-    c2 = workloads.CONFIGS["C2"]
+    c2 = workloads.CONFIGS["w4_bs4096_h4096_e4m3_bf16"]
     assert c2.algorithmic_bytes() == 4096 * 4096 + 4096 * 4096 // 128 * 4 + 1024 * 4096 * 2
 
 

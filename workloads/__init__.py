@@ -76,15 +76,15 @@ class Workload:
 
 # The five workloads of the hot path.
 CONFIGS = {
-    "C1": Workload("C1", 2, 32, 1024, "int8", "f32_group128", "f32",
+    "w2_bs32_h1024_int8_f32": Workload("w2_bs32_h1024_int8_f32", 2, 32, 1024, "int8", "f32_group128", "f32",
                    x_dist="int_uniform", x_param=127, scale_lo=-10, scale_hi=-4),
-    "C2": Workload("C2", 4, 4096, 4096, "e4m3fn", "f32_group128", "bf16",
+    "w4_bs4096_h4096_e4m3_bf16": Workload("w4_bs4096_h4096_e4m3_bf16", 4, 4096, 4096, "e4m3fn", "f32_group128", "bf16",
                    x_dist="normal", x_param=64, scale_lo=-12, scale_hi=-2),
-    "C3": Workload("C3", 8, 8192, 7168, "e5m2", "f32_group128", "bf16",
+    "w8_bs8192_h7168_e5m2_bf16": Workload("w8_bs8192_h7168_e5m2_bf16", 8, 8192, 7168, "e5m2", "f32_group128", "bf16",
                    x_dist="normal", x_param=1024, scale_lo=-16, scale_hi=-4),
-    "C4": Workload("C4", 8, 16384, 8192, "e4m3fn", "e8m0_block32", "bf16",
+    "w8_bs16384_h8192_mx_e4m3_bf16": Workload("w8_bs16384_h8192_mx_e4m3_bf16", 8, 16384, 8192, "e4m3fn", "e8m0_block32", "bf16",
                    x_dist="normal", x_param=32, scale_lo=117, scale_hi=137),
-    "C5": Workload("C5", 8, 65536, 5120, "e5m2", "e8m0_block32", "f32",
+    "w8_bs65536_h5120_mx_e5m2_f32": Workload("w8_bs65536_h5120_mx_e5m2_f32", 8, 65536, 5120, "e5m2", "e8m0_block32", "f32",
                    x_dist="normal", x_param=256, scale_lo=112, scale_hi=142),
 }
 
