@@ -47,7 +47,8 @@ typedef enum qrs_status {
   QRS_OK = 0,
   QRS_ERR_INVALID_ARG = 1, /* a parameter breaks a documented constraint   */
   QRS_ERR_UNSUPPORTED = 2, /* a format the library does not implement      */
-  QRS_ERR_HIP = 3          /* the HIP runtime reported an error at launch  */
+  QRS_ERR_HIP = 3,         /* the HIP runtime reported an error at launch  */
+  QRS_ERR_OUT_OF_MEMORY = 4 /* a host allocation for a plan failed        */
 } qrs_status;
 
 /* Element format of x (page "aclnnQuantReduceScatter", Constraints).
@@ -103,8 +104,9 @@ typedef struct qrs_plan_s* qrs_plan_t;
  *   workspace_bytes_out
  *               receives the device workspace size, always 0 (non-null).
  *
- * Returns QRS_OK, QRS_ERR_INVALID_ARG or QRS_ERR_UNSUPPORTED. On error
- * *plan_out is set to NULL (when plan_out is non-null).
+ * Returns QRS_OK, QRS_ERR_INVALID_ARG, QRS_ERR_UNSUPPORTED or
+ * QRS_ERR_OUT_OF_MEMORY. On error *plan_out is set to NULL (when plan_out is
+ * non-null).
  */
 qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, qrs_scale_layout scale_layout,
                     qrs_out_dtype out_dtype, qrs_plan_t* plan_out, size_t* workspace_bytes_out);

@@ -48,6 +48,7 @@ class Status(IntEnum):
     INVALID_ARG = 1
     UNSUPPORTED = 2
     HIP = 3
+    OUT_OF_MEMORY = 4
 
 
 class XDtype(IntEnum):

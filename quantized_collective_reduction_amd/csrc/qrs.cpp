@@ -77,6 +77,7 @@ const char* qrs_status_string(qrs_status status) {
     case QRS_ERR_INVALID_ARG: return "QRS_ERR_INVALID_ARG";
     case QRS_ERR_UNSUPPORTED: return "QRS_ERR_UNSUPPORTED";
     case QRS_ERR_HIP: return "QRS_ERR_HIP";
+    case QRS_ERR_OUT_OF_MEMORY: return "QRS_ERR_OUT_OF_MEMORY";
   }
   return "QRS_ERR_UNKNOWN";
 }
@@ -108,7 +109,7 @@ qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, 
     return fail(QRS_ERR_INVALID_ARG, "out_dtype %d is not a qrs_out_dtype", static_cast<int>(out_dtype));
 
   qrs_plan_s* p = new (std::nothrow) qrs_plan_s;
-  if (!p) return fail(QRS_ERR_INVALID_ARG, "out of host memory");
+  if (!p) return fail(QRS_ERR_OUT_OF_MEMORY, "out of host memory");
   p->world_size = world_size;
   p->bs = bs;
   p->rows = rows;

@@ -248,3 +248,24 @@ def test_all_shares_rejects_bad_arguments_on_host(lib):
     assert run(A + 4 * G, A + 5 * G, x=bad_x) == qrs.Status.INVALID_ARG  # misaligned x
     bad_s = (ctypes.c_void_p * 2)(A + 2 * G + 2, A + 3 * G)
     assert run(A + 4 * G, A + 5 * G, s=bad_s) == qrs.Status.INVALID_ARG  # misaligned fp32 scales
+
+
+def test_header_compiles_as_c99_and_cxx(tmp_path):
+    """include/qrs.h is a plain C header: it compiles as C99 and as C++,
+    and a C caller can reference every declared entry point."""
+    import shutil
+    import subprocess
+
+    decls = _declared_functions()
+    src = tmp_path / "use.c"
+    src.write_text('#include "qrs.h"\n' + "typedef void (*fn)(void);\n"
+                   + "fn refs[] = {" + ", ".join(f"(fn){d}" for d in decls) + "};\n"
+                   "int main(void) { qrs_status s = QRS_OK; qrs_out_dtype o = QRS_OUT_F16; (void)o; return (int)s; }\n")
+    inc = os.path.dirname(HEADER)
+    gcc = shutil.which("gcc") or shutil.which("cc")
+    gxx = shutil.which("g++") or shutil.which("c++")
+    if gcc is None or gxx is None:
+        pytest.skip("no host C/C++ compiler")
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-fsyntax-only", "-I", inc, str(src)], check=True)
+    subprocess.run([gxx, "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", "-x", "c++", "-I", inc, str(src)],
+                   check=True)
