@@ -15,15 +15,21 @@ from test_oracle_closed_forms import build_example, load_worked_examples
 
 
 def _fold(xs, ss, xf, sl, out, *, order=None, start_zero=False, wide=False, pairwise=False, group=None,
-          to_bf16=fp32_to_bf16_bits, to_f16=fp32_to_f16_bits):
+          to_bf16=fp32_to_bf16_bits, to_f16=fp32_to_f16_bits, scale_col=None, unsigned=False):
     """A configurable re-statement of the definition used only to plant mistakes."""
     g = group or GROUP_SIZE[sl]
     xt = decode_table(xf)
+    if unsigned:
+        xt = np.abs(xt)
     st = scale_decode_table()
     ps = []
     for x, s in zip(xs, ss):
         sv = s if sl == "f32_group128" else st[s]
-        sv = np.repeat(sv, g, axis=1)[:, : x.shape[1]]
+        if scale_col is not None:  # planted: a wrong column -> group map
+            cols = np.arange(x.shape[1])
+            sv = sv[:, scale_col(cols, GROUP_SIZE[sl], sv.shape[1])]
+        else:
+            sv = np.repeat(sv, g, axis=1)[:, : x.shape[1]]
         if sv.shape[1] < x.shape[1]:
             sv = np.tile(sv, (1, x.shape[1] // sv.shape[1] + 1))[:, : x.shape[1]]
         with np.errstate(over="ignore", invalid="ignore"):
@@ -73,6 +79,7 @@ def _worked_examples_pass(fn):
 def _cross_layout_passes(fn):
     rng = np.random.default_rng(3)
     wl = workloads.CONFIGS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=8 * 2, h=1024)
+    # The reference side must itself be the unmutated definition.
     xs, _ = workloads.generate(wl)
     codes128 = [rng.integers(110, 145, size=(wl.rows, wl.h // 128), dtype=np.uint8) for _ in range(8)]
     mx = [np.repeat(c, 4, axis=1) for c in codes128]
@@ -98,6 +105,9 @@ MUTANTS = {
     "bf16_by_truncation": dict(to_bf16=_truncate_bf16),
     "f16_toward_zero": dict(to_f16=_f16_toward_zero),
     "group_of_64_columns": dict(group=64),
+    "scale_of_the_next_group": dict(scale_col=lambda c, g, n: np.minimum(c // g + 1, n - 1)),
+    "scales_indexed_by_column_modulo": dict(scale_col=lambda c, g, n: c % n),
+    "sign_of_x_dropped": dict(unsigned=True),
 }
 
 
