@@ -32,12 +32,25 @@ MODES = [
 ]
 
 
-@pytest.mark.parametrize("name", ["w2_bs32_h1024_int8_f32", "w4_bs4096_h4096_e4m3_bf16", "w8_bs8192_h7168_e5m2_bf16", "w8_bs16384_h8192_mx_e4m3_bf16", "w8_bs65536_h5120_mx_e5m2_f32"])
+@pytest.mark.parametrize("name", sorted(workloads.CONFIGS))
 def test_workload_full_size(gpu, name):
+    """Every element of each workload at full size, with the slices placed
+    as the benchmark places them (one buffer, recommended pitch)."""
+    import quantized_collective_reduction_amd as qrs
+
     wl = workloads.CONFIGS[name]
     log(f"[parity] {name}: W={wl.world_size} BS={wl.bs} H={wl.h} {wl.x_format}/{wl.scale_layout}->{wl.out_dtype}")
     xs, ss = workloads.generate(wl)
-    got = run_gpu(wl.world_size, wl.rows, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype, xs, ss)
+    p = qrs.plan(wl.world_size, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    dx, ds = qrs.alloc_slices(p)
+    for t, a in zip(dx, xs):
+        t.copy_(torch.from_numpy(a))
+    for t, a in zip(ds, ss):
+        t.copy_(torch.from_numpy(a))
+    out = empty_out(wl.rows, wl.h, wl.out_dtype).fill_(float("nan"))
+    qrs.Launch(p, dx, ds, out)()  # the call the benchmark times
+    torch.cuda.synchronize()
+    got = out_bits(out)
     want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype), wl.out_dtype)
     n_diff = assert_parity(got, want, wl.out_dtype, name)
     log(f"[parity] {name}: {got.size} elements, {n_diff} not bit-identical")
