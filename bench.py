@@ -53,7 +53,7 @@ MALL_BYTES = 256 << 20
 def workloads_names():
     import workloads
 
-    return workloads.CONFIGS.keys()
+    return workloads.WORKLOADS.keys()
 
 
 def log(msg):
@@ -232,7 +232,7 @@ def main():
         sys.exit("no GPU visible")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = workloads.CONFIGS[args.workload]
+    wl = workloads.WORKLOADS[args.workload]
     log(f"[bench] {args.op} on {wl.name}: W={wl.world_size} BS={wl.bs} H={wl.h} rows={wl.rows} "
         f"{wl.x_format}/{wl.scale_layout}->{wl.out_dtype}")
     alg_bytes, launches, outs, host_inputs = OPS[args.op](wl, dev, qrs, workloads, torch, args.layout)

@@ -41,7 +41,7 @@ def main():
                  "Written by tests/golden/make_digests.py from workloads.generate and oracle.reduce_scatter_share.",
         "configs": {},
     }
-    for name, wl in workloads.CONFIGS.items():
+    for name, wl in workloads.WORKLOADS.items():
         xs, ss = workloads.generate(wl)
         out = oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype)
         result["configs"][name] = {

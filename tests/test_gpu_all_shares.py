@@ -54,7 +54,7 @@ def test_all_shares_small(gpu, x_format, scale_layout, out_dtype, w):
 def test_all_shares_full_size_sampled(gpu):
     """The W=8, BS=16384, H=8192 MX group (1 GiB of codes) in the launch the
     benchmark times; every share checked on 24 sampled rows, all columns."""
-    wl = workloads.CONFIGS["w8_bs16384_h8192_mx_e4m3_bf16"]
+    wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"]
     log("[all_shares] generating 8 x [16384, 8192] inputs")
     xs, ss = workloads.generate_full(wl)
     got = _run(wl, xs, ss)
@@ -67,7 +67,7 @@ def test_all_shares_full_size_sampled(gpu):
 
 
 def test_all_shares_rejects_overlapping_outputs(gpu):
-    wl = workloads.CONFIGS["w4_bs4096_h4096_e4m3_bf16"].with_(bs=4 * 8)
+    wl = workloads.WORKLOADS["w4_bs4096_h4096_e4m3_bf16"].with_(bs=4 * 8)
     p = qrs.plan(4, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
     xs = [torch.zeros(wl.bs, wl.h, dtype=torch.uint8, device="cuda") for _ in range(4)]
     ss = [torch.zeros(wl.bs, wl.h // 128, dtype=torch.float32, device="cuda") for _ in range(4)]

@@ -32,13 +32,13 @@ MODES = [
 ]
 
 
-@pytest.mark.parametrize("name", sorted(workloads.CONFIGS))
+@pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
 def test_workload_full_size(gpu, name):
     """Every element of each workload at full size, with the slices placed
     as the benchmark places them (one buffer, recommended pitch)."""
     import quantized_collective_reduction_amd as qrs
 
-    wl = workloads.CONFIGS[name]
+    wl = workloads.WORKLOADS[name]
     log(f"[parity] {name}: W={wl.world_size} BS={wl.bs} H={wl.h} {wl.x_format}/{wl.scale_layout}->{wl.out_dtype}")
     xs, ss = workloads.generate(wl)
     p = qrs.plan(wl.world_size, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
@@ -83,7 +83,7 @@ def test_sweep_small_ragged(gpu, x_format, scale_layout, out_dtype, w, h):
 
 @pytest.mark.parametrize("rows", [1, 2, 7, 63, 64, 65, 257])
 def test_row_counts_around_block_edges(gpu, rows):
-    wl = workloads.CONFIGS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=8 * rows, h=1152)
+    wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=8 * rows, h=1152)
     xs, ss = workloads.generate(wl)
     got = run_gpu(8, rows, 1152, wl.x_format, wl.scale_layout, "f32", xs, ss)
     want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, "f32"), "f32")
@@ -114,7 +114,7 @@ def test_slices_in_separate_allocations_and_one_buffer(gpu):
     [W, rows, H] buffer, give the same bits."""
     import quantized_collective_reduction_amd as qrs
 
-    wl = workloads.CONFIGS["w8_bs8192_h7168_e5m2_bf16"].with_(bs=8 * 40, h=2048)
+    wl = workloads.WORKLOADS["w8_bs8192_h7168_e5m2_bf16"].with_(bs=8 * 40, h=2048)
     xs, ss = workloads.generate(wl)
     p = qrs.plan(8, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
     dx, ds = to_device(xs, ss)
@@ -136,7 +136,7 @@ def test_runs_on_the_given_stream(gpu):
     """The kernel is ordered after earlier work on a non-default stream."""
     import quantized_collective_reduction_amd as qrs
 
-    wl = workloads.CONFIGS["w4_bs4096_h4096_e4m3_bf16"].with_(bs=4 * 256)
+    wl = workloads.WORKLOADS["w4_bs4096_h4096_e4m3_bf16"].with_(bs=4 * 256)
     xs, ss = workloads.generate(wl)
     want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype), wl.out_dtype)
     p = qrs.plan(4, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
@@ -191,7 +191,7 @@ def test_prepared_launch_matches_run(gpu):
     """qrs.Launch (arguments marshalled once) gives the same bits as qrs.run."""
     import quantized_collective_reduction_amd as qrs
 
-    wl = workloads.CONFIGS["w8_bs65536_h5120_mx_e5m2_f32"].with_(bs=8 * 33)
+    wl = workloads.WORKLOADS["w8_bs65536_h5120_mx_e5m2_f32"].with_(bs=8 * 33)
     xs, ss = workloads.generate(wl)
     p = qrs.plan(8, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
     dx, ds = to_device(xs, ss)
@@ -213,7 +213,7 @@ def test_recommended_slice_placement(gpu, full):
     the oracle's bits, for this GPU's share and for all shares."""
     import quantized_collective_reduction_amd as qrs
 
-    wl = workloads.CONFIGS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=8 * 12, h=2048)
+    wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=8 * 12, h=2048)
     p = qrs.plan(8, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
     xs, ss = workloads.generate_full(wl) if full else workloads.generate(wl)
     dx, ds = qrs.alloc_slices(p, full_inputs=full)

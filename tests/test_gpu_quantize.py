@@ -95,7 +95,7 @@ def test_every_in_range_bf16_value_converts_like_the_oracle(gpu, x_format, scale
 def test_quantize_full_size_sampled(gpu, x_format, scale_layout):
     """One rank's [16384, 8192] activations, the launch the benchmark times;
     256 sampled tokens compared bit for bit."""
-    wl = workloads.CONFIGS["w8_bs16384_h8192_mx_e4m3_bf16"]
+    wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"]
     bits = workloads.generate_activations(wl, 0)
     gc, gs = _gpu_quantize(bits, x_format, scale_layout)
     rows = np.sort(np.random.default_rng(9).choice(wl.bs, 256, replace=False))
@@ -112,7 +112,7 @@ def test_producer_to_reduce_scatter_pipeline(gpu, x_format, scale_layout, out_dt
     bit-exact with the oracle's quantize -> all_shares, and close to the exact
     reduce-scatter of the unquantized values."""
     w, bs, h = 4, 4 * 6, 2048
-    wl = workloads.CONFIGS["w4_bs4096_h4096_e4m3_bf16"].with_(world_size=w, bs=bs, h=h)
+    wl = workloads.WORKLOADS["w4_bs4096_h4096_e4m3_bf16"].with_(world_size=w, bs=bs, h=h)
     acts = [workloads.generate_activations(wl, r) for r in range(w)]
     g = 128 if scale_layout == "f32_group128" else 32
     dx, ds = [], []

@@ -47,7 +47,7 @@ def test_grand_total_is_exact():
 
 
 def test_share_depends_only_on_its_row_block():
-    wl = workloads.CONFIGS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=4 * 3, world_size=4, h=1024)
+    wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=4 * 3, world_size=4, h=1024)
     xs, ss = workloads.generate_full(wl)
     base = all_shares(xs, ss, wl.x_format, wl.scale_layout, "f32")
     xs2 = [x.copy() for x in xs]
@@ -73,7 +73,7 @@ def test_received_slices_are_in_rank_order():
 
 def test_single_block_equals_share():
     """With the all-to-all done by hand, the result is reduce_scatter_share."""
-    wl = workloads.CONFIGS["w8_bs65536_h5120_mx_e5m2_f32"].with_(bs=8 * 2, h=1024)
+    wl = workloads.WORKLOADS["w8_bs65536_h5120_mx_e5m2_f32"].with_(bs=8 * 2, h=1024)
     xs, ss = workloads.generate_full(wl)
     outs = all_shares(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype)
     g = GROUP_SIZE[wl.scale_layout]

@@ -113,7 +113,7 @@ def _negate_codes(x, x_format):
 
 @pytest.mark.parametrize("x_format,scale_layout", [("int8", "f32_group128"), ("e4m3fn", "e8m0_block32"), ("e5m2", "f32_group128")])
 def test_opposite_rank_pairs_cancel_to_positive_zero(x_format, scale_layout):
-    wl = workloads.CONFIGS["w4_bs4096_h4096_e4m3_bf16"].with_(world_size=2, bs=8, h=1024, x_format=x_format, scale_layout=scale_layout,
+    wl = workloads.WORKLOADS["w4_bs4096_h4096_e4m3_bf16"].with_(world_size=2, bs=8, h=1024, x_format=x_format, scale_layout=scale_layout,
                                        x_dist="int_uniform" if x_format == "int8" else "normal",
                                        x_param=127 if x_format == "int8" else 16,
                                        scale_lo=100 if scale_layout == "e8m0_block32" else -6,
@@ -134,7 +134,7 @@ def test_scale_influence_is_local_to_its_group():
     does change some of them."""
     for scale_layout in ("f32_group128", "e8m0_block32"):
         g = GROUP_SIZE[scale_layout]
-        wl = workloads.CONFIGS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=4 * 6, world_size=4, h=1024, scale_layout=scale_layout,
+        wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=4 * 6, world_size=4, h=1024, scale_layout=scale_layout,
                                            scale_lo=-4 if scale_layout == "f32_group128" else 120,
                                            scale_hi=4 if scale_layout == "f32_group128" else 134, out_dtype="f32")
         xs, ss = workloads.generate(wl)
@@ -157,7 +157,7 @@ def test_mx_and_group_layouts_agree_on_equal_scales():
     scales 2^(code-127) per 128-group: the two layouts index the same
     columns."""
     rng = np.random.default_rng(3)
-    wl = workloads.CONFIGS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=8 * 4, h=2048)
+    wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=8 * 4, h=2048)
     xs, _ = workloads.generate(wl)
     codes128 = [rng.integers(110, 145, size=(wl.rows, wl.h // 128), dtype=np.uint8) for _ in range(8)]
     mx = [np.repeat(c, 4, axis=1) for c in codes128]
@@ -168,7 +168,7 @@ def test_mx_and_group_layouts_agree_on_equal_scales():
 
 
 def test_rows_are_independent():
-    wl = workloads.CONFIGS["w8_bs8192_h7168_e5m2_bf16"].with_(bs=8 * 16, h=1024)
+    wl = workloads.WORKLOADS["w8_bs8192_h7168_e5m2_bf16"].with_(bs=8 * 16, h=1024)
     xs, ss = workloads.generate(wl)
     perm = np.random.default_rng(0).permutation(wl.rows)
     a = reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, "f32")
@@ -192,7 +192,7 @@ def test_non_finite_propagation():
 
 
 def test_16bit_outputs_are_rounded_fp32_output():
-    wl = workloads.CONFIGS["w4_bs4096_h4096_e4m3_bf16"].with_(bs=4 * 8)
+    wl = workloads.WORKLOADS["w4_bs4096_h4096_e4m3_bf16"].with_(bs=4 * 8)
     xs, ss = workloads.generate(wl)
     f = reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, "f32")
     b = reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, "bf16")
@@ -212,7 +212,7 @@ def test_error_bound_against_exact_sum(name):
     u = 2^-24 (recursive summation of W rounded products; Higham, Accuracy and
     Stability of Numerical Algorithms, the dot-product bound of ch. 3). Checked
     on sampled elements of a few rows of each workload's distribution."""
-    wl = workloads.CONFIGS[name]
+    wl = workloads.WORKLOADS[name]
     wl = wl.with_(bs=wl.world_size * 4)
     xs, ss = workloads.generate(wl)
     y = reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, "f32")

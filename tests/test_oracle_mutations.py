@@ -78,7 +78,7 @@ def _worked_examples_pass(fn):
 
 def _cross_layout_passes(fn):
     rng = np.random.default_rng(3)
-    wl = workloads.CONFIGS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=8 * 2, h=1024)
+    wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=8 * 2, h=1024)
     # The reference side must itself be the unmutated definition.
     xs, _ = workloads.generate(wl)
     codes128 = [rng.integers(110, 145, size=(wl.rows, wl.h // 128), dtype=np.uint8) for _ in range(8)]

@@ -14,11 +14,11 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "digests.json")
 
 
 def _small(name):
-    wl = workloads.CONFIGS[name]
+    wl = workloads.WORKLOADS[name]
     return wl.with_(bs=wl.world_size * 8)
 
 
-@pytest.mark.parametrize("name", sorted(workloads.CONFIGS))
+@pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
 def test_deterministic_and_shaped(name):
     wl = _small(name)
     xs, ss = workloads.generate(wl)
@@ -36,7 +36,7 @@ def test_deterministic_and_shaped(name):
     assert not np.array_equal(xs[0], xs[1])
 
 
-@pytest.mark.parametrize("name", sorted(workloads.CONFIGS))
+@pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
 def test_value_ranges(name):
     wl = _small(name)
     xs, ss = workloads.generate(wl)
@@ -57,15 +57,15 @@ def test_value_ranges(name):
 
 def test_algorithmic_bytes_match_the_size_formulas():
     # x: BS*H bytes over all ranks' slices; scales: BS*H/128*4 or BS*H/32*1.
-    c4 = workloads.CONFIGS["w8_bs16384_h8192_mx_e4m3_bf16"]
+    c4 = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"]
     assert c4.algorithmic_bytes() == 16384 * 8192 + 16384 * 8192 // 32 + 2048 * 8192 * 2 == 171_966_464
-    c5 = workloads.CONFIGS["w8_bs65536_h5120_mx_e5m2_f32"]
+    c5 = workloads.WORKLOADS["w8_bs65536_h5120_mx_e5m2_f32"]
     assert c5.algorithmic_bytes() == 65536 * 5120 + 65536 * 5120 // 32 + 8192 * 5120 * 4 == 513_802_240
-    c2 = workloads.CONFIGS["w4_bs4096_h4096_e4m3_bf16"]
+    c2 = workloads.WORKLOADS["w4_bs4096_h4096_e4m3_bf16"]
     assert c2.algorithmic_bytes() == 4096 * 4096 + 4096 * 4096 // 128 * 4 + 1024 * 4096 * 2
 
 
-@pytest.mark.parametrize("name", sorted(workloads.CONFIGS))
+@pytest.mark.parametrize("name", sorted(workloads.WORKLOADS))
 def test_inputs_match_stored_digests(name):
     import sys
 
@@ -74,5 +74,5 @@ def test_inputs_match_stored_digests(name):
 
     with open(GOLDEN) as f:
         want = json.load(f)["configs"][name]["inputs_sha256"]
-    xs, ss = workloads.generate(workloads.CONFIGS[name])
+    xs, ss = workloads.generate(workloads.WORKLOADS[name])
     assert input_digest(xs, ss) == want

@@ -75,7 +75,7 @@ class Workload:
 
 
 # The five workloads of the hot path.
-CONFIGS = {
+WORKLOADS = {
     "w2_bs32_h1024_int8_f32": Workload("w2_bs32_h1024_int8_f32", 2, 32, 1024, "int8", "f32_group128", "f32",
                    x_dist="int_uniform", x_param=127, scale_lo=-10, scale_hi=-4),
     "w4_bs4096_h4096_e4m3_bf16": Workload("w4_bs4096_h4096_e4m3_bf16", 4, 4096, 4096, "e4m3fn", "f32_group128", "bf16",
