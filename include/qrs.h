@@ -28,7 +28,10 @@
  * Ownership: the caller owns every device buffer and the stream; the library
  * owns only the plan. No call allocates device memory; the workspace size is
  * always 0. A plan is immutable and may be used by any number of concurrent
- * qrs_run calls on different streams.
+ * qrs_run calls on different streams. The launching calls (qrs_run,
+ * qrs_run_all_shares, qrs_run_strided, qrs_quantize) enqueue kernels only --
+ * no allocation, memset or synchronisation -- so they may be captured in a
+ * HIP graph.
  *
  * Errors: every call returns a qrs_status. On failure, qrs_last_error()
  * returns a human-readable message for the calling thread.
