@@ -248,6 +248,12 @@ qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t
   const int64_t g = f32_scales ? 128 : 32;
   const int64_t sb = f32_scales ? 4 : 1;
   const int64_t ob = plan->out_format == qrs::kOutF32 ? 4 : 2;
+  // Every address the kernel forms must stay well inside 64 bits: bound the
+  // byte extent of each tensor (rows - 1 strides plus one row) by 2^48.
+  // Compare before multiplying so the check itself cannot overflow.
+  const int64_t limit = int64_t{1} << 48;
+  if (x_row_stride > limit / rows || scale_row_stride > limit / rows / sb || out_row_stride > limit / rows / ob)
+    return fail(QRS_ERR_INVALID_ARG, "row stride too large for %lld rows", static_cast<long long>(rows));
   if (x_row_stride < h || x_row_stride % 16)
     return fail(QRS_ERR_INVALID_ARG, "x_row_stride %lld: must be >= h and a multiple of 16 bytes",
                 static_cast<long long>(x_row_stride));
@@ -257,8 +263,6 @@ qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t
   if (out_row_stride < h || (out_row_stride * ob) % 16)
     return fail(QRS_ERR_INVALID_ARG, "out_row_stride %lld: must be >= h and span a multiple of 16 bytes",
                 static_cast<long long>(out_row_stride));
-  if (x_row_stride > (int64_t{1} << 40) || scale_row_stride > (int64_t{1} << 40) || out_row_stride > (int64_t{1} << 40))
-    return fail(QRS_ERR_INVALID_ARG, "row stride too large");
   if (!aligned(out, 16)) return fail(QRS_ERR_INVALID_ARG, "out is not 16-byte aligned");
   // Extents actually addressed (last row ends at its h-th element).
   const uint64_t x_span = static_cast<uint64_t>((rows - 1) * x_row_stride + h);

@@ -119,8 +119,8 @@ __device__ __forceinline__ float group_max(float v) {
 }
 
 template <int XF, int SL>
-__device__ __forceinline__ void quantize_piece(const u32x4* __restrict__ in, u32x2* __restrict__ codes,
-                                               void* __restrict__ scales, uint64_t t, bool active, u32x4 w);
+__device__ __forceinline__ void quantize_piece(u32x2* __restrict__ codes, void* __restrict__ scales, uint64_t t,
+                                               bool active, u32x4 w);
 
 template <int XF, int SL>
 __global__ __launch_bounds__(kBlock) void quantize_kernel(const u32x4* __restrict__ in, u32x2* __restrict__ codes,
@@ -139,16 +139,18 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(const u32x4* __restric
 #pragma unroll
   for (int j = 0; j < P; ++j) {
     const uint64_t t = block_first + static_cast<uint64_t>(j) * kBlock + threadIdx.x;
-    quantize_piece<XF, SL>(in, codes, scales, t, t < n_lanes, w[j]);
+    quantize_piece<XF, SL>(codes, scales, t, t < n_lanes, w[j]);
   }
 }
 
+// One 8-element piece: decode the bf16 pair words, combine the group
+// maximum, pick the scale, encode, store (codes, and the scale from the
+// group's first lane).
 template <int XF, int SL>
-__device__ __forceinline__ void quantize_piece(const u32x4* __restrict__ in, u32x2* __restrict__ codes,
-                                               void* __restrict__ scales, uint64_t t, bool active, u32x4 w) {
+__device__ __forceinline__ void quantize_piece(u32x2* __restrict__ codes, void* __restrict__ scales, uint64_t t,
+                                               bool active, u32x4 w) {
   constexpr int G = SL == kScaleF32Group128 ? 128 : 32;
   constexpr int L = G / kElemsPerLane;  // lanes per group
-  (void)in;
   float v[kElemsPerLane];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {

@@ -18,6 +18,18 @@ def lib():
     return qrs.load_library()
 
 
+@pytest.fixture(scope="module")
+def fake_ptr_lib(lib):
+    """For tests that hand fake device addresses to calls expected to fail
+    their host checks: run them only where no GPU is visible, so a missing
+    check could never launch a kernel on such an address."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("fake-address checks run only without a GPU")
+    return lib
+
+
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
@@ -113,7 +125,8 @@ def _run_raw(lib, p, xs, ss, out):
     return lib.qrs_run(p.handle if p else None, xa, sa, out, None, 0, None)
 
 
-def test_run_rejects_bad_pointers_on_host(lib):
+def test_run_rejects_bad_pointers_on_host(fake_ptr_lib):
+    lib = fake_ptr_lib
     p = qrs.plan(2, 32, 1024, "e4m3fn", "f32_group128", "f32")
     n = p.rows * p.h
     A = 1 << 40  # fake, never dereferenced: every call below fails its host checks
@@ -133,7 +146,8 @@ def test_run_rejects_bad_pointers_on_host(lib):
     assert b"overlaps" in lib.qrs_last_error()
 
 
-def test_stream_copy_rejects_bad_arguments_on_host(lib):
+def test_stream_copy_rejects_bad_arguments_on_host(fake_ptr_lib):
+    lib = fake_ptr_lib
     A = 1 << 40
     assert lib.qrs_stream_copy(None, A, 16, None) == qrs.Status.INVALID_ARG
     assert lib.qrs_stream_copy(A, A + 4096, 0, None) == qrs.Status.INVALID_ARG
@@ -170,7 +184,8 @@ def test_prepared_launch_checks_arguments_on_host(lib):
         qrs.Launch(p, x, s, torch.zeros(16, 1024, dtype=torch.float32))  # wrong output size
 
 
-def test_strided_run_rejects_bad_strides_on_host(lib):
+def test_strided_run_rejects_bad_strides_on_host(fake_ptr_lib):
+    lib = fake_ptr_lib
     p = qrs.plan(2, 32, 1024, "e4m3fn", "e8m0_block32", "f32")
     A = 1 << 40
     xs = (ctypes.c_void_p * 2)(A, A + (1 << 30))
@@ -203,7 +218,8 @@ def test_slice_pitch(lib):
     assert lib.qrs_slice_pitch(p.handle, 2, None, None) == qrs.Status.INVALID_ARG
 
 
-def test_quantize_rejects_bad_arguments_on_host(lib):
+def test_quantize_rejects_bad_arguments_on_host(fake_ptr_lib):
+    lib = fake_ptr_lib
     A = 1 << 40
     x, c, s = A, A + (1 << 30), A + (2 << 30)
 
@@ -227,7 +243,8 @@ def test_quantize_rejects_bad_arguments_on_host(lib):
     assert b"overlap" in lib.qrs_last_error()
 
 
-def test_all_shares_rejects_bad_arguments_on_host(lib):
+def test_all_shares_rejects_bad_arguments_on_host(fake_ptr_lib):
+    lib = fake_ptr_lib
     p = qrs.plan(2, 32, 1024, "e4m3fn", "f32_group128", "bf16")
     A = 1 << 40
     G = 1 << 30
@@ -269,3 +286,18 @@ def test_header_compiles_as_c99_and_cxx(tmp_path):
     subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-pedantic", "-fsyntax-only", "-I", inc, str(src)], check=True)
     subprocess.run([gxx, "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", "-x", "c++", "-I", inc, str(src)],
                    check=True)
+
+
+def test_strided_run_rejects_address_overflow(fake_ptr_lib):
+    lib = fake_ptr_lib
+    p = qrs.plan(2, 2 * 65536, 1024, "e4m3fn", "e8m0_block32", "f32")
+    A = 1 << 40
+    xs = (ctypes.c_void_p * 2)(A, A + (1 << 30))
+    ss = (ctypes.c_void_p * 2)(A + (2 << 30), A + (3 << 30))
+    huge = (1 << 62) // 16 * 16  # (rows - 1) * stride would overflow 64 bits
+    assert lib.qrs_run_strided(p.handle, xs, huge, ss, 32, A + (4 << 30), 1024, None, 0, None) == \
+        qrs.Status.INVALID_ARG
+    assert lib.qrs_run_strided(p.handle, xs, 1024, ss, 1 << 60, A + (4 << 30), 1024, None, 0, None) == \
+        qrs.Status.INVALID_ARG
+    assert lib.qrs_run_strided(p.handle, xs, 1024, ss, 32, A + (4 << 30), 1 << 61, None, 0, None) == \
+        qrs.Status.INVALID_ARG
