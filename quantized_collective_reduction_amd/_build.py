@@ -60,5 +60,25 @@ def build(out_path: str = LIB_PATH, defines=(), verbose: bool = False) -> str:
     return out_path
 
 
+C_ABI_DRIVER_SRC = os.path.join(REPO_ROOT, "tests", "c_abi", "run_share.cpp")
+C_ABI_DRIVER = os.path.join(REPO_ROOT, "tests", "c_abi", "run_share")
+
+
+def build_c_abi_driver(verbose: bool = False) -> str:
+    """Compile the C++ caller used by the tests to exercise the C ABI without
+    Python. Links libqrs.so from the package directory (rpath relative to the
+    executable)."""
+    rel = os.path.relpath(PKG_DIR, os.path.dirname(C_ABI_DRIVER))
+    cmd = [hipcc(), "-O2", "-std=c++17", "-I", INCLUDE, C_ABI_DRIVER_SRC, "-L", PKG_DIR, "-lqrs",
+           f"-Wl,-rpath,$ORIGIN/{rel}", "-o", C_ABI_DRIVER]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+    return C_ABI_DRIVER
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_c_abi_driver(verbose="-v" in sys.argv))
