@@ -44,6 +44,7 @@ METRIC = "achieved HBM GB/s and % of peak for dequant+reduce at W=8, H=8192"
 # for the source it was measured on).
 KERNEL_SOURCES = {
     "share": "quantized_collective_reduction_amd/csrc/qrs_kernels.hip",
+    "strided": "quantized_collective_reduction_amd/csrc/qrs_kernels.hip",
     "all_shares": "quantized_collective_reduction_amd/csrc/qrs_kernels.hip",
     "quantize": "quantized_collective_reduction_amd/csrc/qrs_quantize.hip",
 }
@@ -150,6 +151,31 @@ def setup_share(wl, dev, qrs, workloads, torch, layout):
     return alg_bytes, launches, outs, (xs, ss)
 
 
+def setup_strided(wl, dev, qrs, workloads, torch, layout):
+    """This GPU's share from a row-interleaved receive buffer
+    (qrs_run_strided): codes [rows, W, H] and scales [rows, W, H/G], so each
+    rank slice is a row-strided view; output [rows, H]."""
+    alg_bytes = wl.algorithmic_bytes()
+    t0 = time.perf_counter()
+    xs, ss = workloads.generate(wl)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+    n_sets = max(2, -(-4 * MALL_BYTES // alg_bytes))
+    out_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.out_dtype]
+    p = qrs.plan(wl.world_size, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    stream = torch.cuda.current_stream(dev)
+    bx0 = torch.from_numpy(np.ascontiguousarray(np.stack(xs, axis=1))).to(dev)
+    bs0 = torch.from_numpy(np.ascontiguousarray(np.stack(ss, axis=1))).to(dev)
+    launches, outs = [], []
+    for k in range(n_sets):
+        bx = bx0 if k == 0 else bx0.clone()
+        bs_ = bs0 if k == 0 else bs0.clone()
+        out = torch.empty((wl.rows, wl.h), dtype=out_dt, device=dev)
+        launches.append(qrs.StridedLaunch(p, [bx[:, r] for r in range(wl.world_size)],
+                                          [bs_[:, r] for r in range(wl.world_size)], out, stream=stream))
+        outs.append([out])
+    return alg_bytes, launches, outs, (xs, ss)
+
+
 def setup_all_shares(wl, dev, qrs, workloads, torch, layout):
     """The group's whole reduce-scatter on this GPU (qrs_run_all_shares):
     W inputs [BS, H] -> W shares [BS/W, H], the all-to-all by addressing."""
@@ -194,7 +220,7 @@ def setup_quantize(wl, dev, qrs, workloads, torch, layout):
     return alg_bytes, launches, outs, None
 
 
-OPS = {"share": setup_share, "all_shares": setup_all_shares, "quantize": setup_quantize}
+OPS = {"share": setup_share, "strided": setup_strided, "all_shares": setup_all_shares, "quantize": setup_quantize}
 
 
 def main():
@@ -205,9 +231,10 @@ def main():
     ap.add_argument("--workload", default="w8_bs16384_h8192_mx_e4m3_bf16", choices=sorted(workloads_names()),
                     help="default: the W=8, BS=16384, H=8192 MX E4M3FN -> bf16 share")
     ap.add_argument("--op", default="share", choices=sorted(OPS),
-                    help="share: this GPU's share (the hot path, default); all_shares: every rank's share "
-                         "from the inputs before the all-to-all, in one launch; quantize: the producer-side "
-                         "quantization of one rank's bf16 activations [BS, H]")
+                    help="share: this GPU's share (the hot path, default); strided: the same share from a "
+                         "row-interleaved receive buffer [rows, W, H] through qrs_run_strided; all_shares: every "
+                         "rank's share from the inputs before the all-to-all, in one launch; quantize: the "
+                         "producer-side quantization of one rank's bf16 activations [BS, H]")
     ap.add_argument("--layout", default="pitched", choices=["pitched", "packed", "separate"],
                     help="placement of the W rank slices: pitched (one buffer, the pitch qrs_slice_pitch "
                          "recommends; default), packed (one buffer, back to back), separate (one allocation each)")
@@ -293,7 +320,8 @@ def main():
     achieved = alg_bytes / avg_launch_s / 1e9
     value = alg_bytes * args.steps / wall / 1e9
     result = {
-        "metric": {"share": METRIC, "all_shares": METRIC + " (all W shares in one launch)",
+        "metric": {"share": METRIC, "strided": METRIC + " (row-interleaved receive buffer)",
+                   "all_shares": METRIC + " (all W shares in one launch)",
                "quantize": "achieved HBM GB/s and % of peak for the producer-side quantization"}[args.op],
         "value": round(value, 2),
         "unit": "GB/s",
@@ -309,10 +337,11 @@ def main():
         "config": {
             "workload": f"{wl.name}: W={wl.world_size} BS={wl.bs} H={wl.h} x={wl.x_format} "
                         f"scales={wl.scale_layout} out={wl.out_dtype}"
-                        + {"share": "", "all_shares": ", all W shares from the pre-all-to-all inputs",
+                        + {"share": "", "strided": ", slices row-interleaved in one [rows, W, H] buffer",
+                           "all_shares": ", all W shares from the pre-all-to-all inputs",
                            "quantize": f", quantize one rank's bf16 [{wl.bs}, {wl.h}]"}[args.op],
             "op": args.op,
-            "layout": args.layout if args.op != "quantize" else None,
+            "layout": {"quantize": None, "strided": "row-interleaved"}.get(args.op, args.layout),
             "world_size": wl.world_size,
             "bs": wl.bs,
             "rows": wl.rows,

@@ -183,9 +183,11 @@ qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const 
  *   out_row_stride    elements, >= h, spanning a multiple of 16 bytes; out
  *                     16-byte aligned.
  *
- * The output's address span, from its first to the last element written,
- * must not overlap the address span of any input slice. Errors as for
- * qrs_run.
+ * Each row stride, in bytes, must be below 4 GiB, the plan's rows per
+ * share below 2^32, and one slice's scales, from its first row's start to
+ * its last row's end, must span less than 4 GiB. The output's address span, from its first to the last
+ * element written, must not overlap the address span of any input slice.
+ * Errors as for qrs_run.
  */
 qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t x_row_stride,
                            const void* const* scale_slices, int64_t scale_row_stride, void* out,

@@ -368,6 +368,33 @@ class Launch:
             _check(status)
 
 
+class StridedLaunch:
+    """``run_strided`` with its arguments marshalled once."""
+
+    def __init__(self, p: Plan, x_slices, scale_slices, out, stream=None):
+        lib = load_library()
+        w = p.world_size
+        if len(x_slices) != w or len(scale_slices) != w:
+            raise ValueError(f"need {w} x slices and {w} scale slices")
+        self._ld_x = _row_stride(x_slices, p.rows, p.h, "x slices") * x_slices[0].element_size()
+        self._ld_s = _row_stride(scale_slices, p.rows, p.h // p.group, "scale slices")
+        self._ld_o = _row_stride([out], p.rows, p.h, "out")
+        self._plan = p
+        self._keep = (list(x_slices), list(scale_slices), out)
+        self._xs = (ctypes.c_void_p * w)(*[t.data_ptr() for t in x_slices])
+        self._ss = (ctypes.c_void_p * w)(*[t.data_ptr() for t in scale_slices])
+        self._out = ctypes.c_void_p(out.data_ptr())
+        self._stream = ctypes.c_void_p(_stream_handle(stream))
+        self._fn = lib.qrs_run_strided
+        self._handle = p.handle
+
+    def __call__(self):
+        status = self._fn(self._handle, self._xs, self._ld_x, self._ss, self._ld_s, self._out, self._ld_o, None, 0,
+                          self._stream)
+        if status:
+            _check(status)
+
+
 class AllSharesLaunch:
     """``run_all_shares`` with its arguments marshalled once."""
 

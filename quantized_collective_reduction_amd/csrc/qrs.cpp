@@ -254,6 +254,11 @@ qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t
   const int64_t limit = int64_t{1} << 48;
   if (x_row_stride > limit / rows || scale_row_stride > limit / rows / sb || out_row_stride > limit / rows / ob)
     return fail(QRS_ERR_INVALID_ARG, "row stride too large for %lld rows", static_cast<long long>(rows));
+  // The kernel forms each row's offset as a 32 x 32-bit product.
+  const int64_t stride_limit = int64_t{1} << 32;
+  if (rows >= stride_limit) return fail(QRS_ERR_INVALID_ARG, "%lld rows: must be below 2^32", static_cast<long long>(rows));
+  if (x_row_stride >= stride_limit || scale_row_stride * sb >= stride_limit || out_row_stride * ob >= stride_limit)
+    return fail(QRS_ERR_INVALID_ARG, "row strides must be below 4 GiB");
   if (x_row_stride < h || x_row_stride % 16)
     return fail(QRS_ERR_INVALID_ARG, "x_row_stride %lld: must be >= h and a multiple of 16 bytes",
                 static_cast<long long>(x_row_stride));
@@ -268,6 +273,8 @@ qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t
   const uint64_t x_span = static_cast<uint64_t>((rows - 1) * x_row_stride + h);
   const uint64_t s_span = static_cast<uint64_t>(((rows - 1) * scale_row_stride + h / g) * sb);
   const uint64_t o_span = static_cast<uint64_t>(((rows - 1) * out_row_stride + h) * ob);
+  if (s_span >= (uint64_t{1} << 32))
+    return fail(QRS_ERR_INVALID_ARG, "the scale rows of one slice must span less than 4 GiB");
 
   qrs::ReduceLaunch l;
   std::memset(&l, 0, sizeof(l));

@@ -141,18 +141,39 @@ __device__ __forceinline__ float load_scale(const void* base, uint64_t chunk) {
   }
 }
 
+// Byte offset, within a scale row, of the scale of chunk `chunk` of that row.
+template <int SL>
+__device__ __forceinline__ uint64_t scale_byte_offset(uint64_t chunk) {
+  return SL == kScaleF32Group128 ? (chunk >> 3) * sizeof(float) : (chunk >> 1);
+}
+
+template <int SL>
+__device__ __forceinline__ float load_scale_at(const char* p) {
+  if constexpr (SL == kScaleF32Group128) {
+    return *reinterpret_cast<const float*>(p);
+  } else {
+    return decode_e8m0(*reinterpret_cast<const uint8_t*>(p));
+  }
+}
+
 struct KernelArgs {
   const u32x4* x[kMaxWorld];
   const void* scales[kMaxWorld];
   void* out[kMaxWorld];  // one per share (blockIdx.y)
-  // The share is n_rows rows of chunks_per_row chunks; a row is covered by
-  // blocks_per_row consecutive blocks. Contiguous shares are one row of all
-  // their chunks (row strides unused).
+  // The share is n_rows rows of chunks_per_row chunks. Contiguous shares are
+  // one row of all their chunks (row strides unused). Row-strided shares are
+  // numbered as one flat range of total_chunks chunks, like contiguous ones;
+  // each lane splits its chunk index into (row, column) by multiplication:
+  // div_magic = ceil(2^64 / chunks_per_row) for the block's first chunk,
+  // div_m20 = ceil(2^20 / chunks_per_row) for the lane's short offset from
+  // it (both exact for the ranges the launch admits).
   uint64_t chunks_per_row;
-  uint32_t blocks_per_row;
-  uint64_t x_row_stride;      // in 16-byte units
-  uint64_t scale_row_stride;  // in bytes
-  uint64_t out_row_stride;    // in 16-byte units
+  uint64_t total_chunks;
+  uint64_t div_magic;
+  uint32_t div_m20;
+  uint32_t x_row_stride;      // in 16-byte units
+  uint32_t scale_row_stride;  // in bytes
+  uint32_t out_row_stride;    // in 16-byte units
   uint64_t x_share_stride;      // in 16-byte units
   uint64_t scale_share_stride;  // in bytes
 };
@@ -241,45 +262,88 @@ __device__ __forceinline__ void pack_chunk(const float (&acc)[kChunk], u32x4 (&p
 // Addressing of a launch: one contiguous share (no per-block offset
 // arithmetic: the hot path), one share with row-strided slices and output,
 // or all W shares of contiguous pre-all-to-all inputs (blockIdx.y = share).
-enum Addr : int { kAddrFlat = 0, kAddrRows = 1, kAddrShares = 2 };
+// kAddrFlat32 is the contiguous share when every slice, scale slice and the
+// output span less than 4 GiB: each lane then forms one 32-bit byte offset
+// per tensor kind and every load and store takes the rank's base address
+// from scalar registers (fewer vector instructions and registers).
+enum Addr : int { kAddrFlat = 0, kAddrRows = 1, kAddrShares = 2, kAddrFlat32 = 3 };
 
 template <int W, int XF, int SL, int OF, int ADDR>
 __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
   constexpr bool ROWS = ADDR == kAddrRows;
   constexpr bool SHARES = ADDR == kAddrShares;
+  constexpr bool OFF32 = ADDR == kAddrFlat32;
   constexpr int CH = QRS_CHUNKS_PER_LANE;
   constexpr int P = OutPieces<OF>::kCount;
+  static_assert(!ROWS || CH <= 2, "row split assumes a lane's offset from its block's first chunk < 1024");
   uint32_t block_id = blockIdx.x;
 #if QRS_XCD_REMAP
   if ((gridDim.x & 7u) == 0) block_id = (block_id & 7u) * (gridDim.x >> 3) + (block_id >> 3);
 #endif
-  // Row and first chunk of this block (uniform). Chunk j of this lane is
-  // base + j*QRS_BLOCK within the row: every load instruction of a wave
-  // covers one contiguous range.
-  const uint32_t row = ROWS ? block_id / a.blocks_per_row : 0u;
-  const uint64_t block_first = static_cast<uint64_t>(block_id - row * a.blocks_per_row) * (QRS_BLOCK * CH);
+  // First chunk of this block (uniform). Chunk j of this lane is
+  // base + j*QRS_BLOCK: every load instruction of a wave covers one
+  // contiguous range of chunks (for row-strided shares, one contiguous range
+  // per row it touches).
+  const uint64_t block_first = static_cast<uint64_t>(block_id) * (QRS_BLOCK * CH);
   const uint64_t base = block_first + threadIdx.x;
-  const uint64_t n_chunks = a.chunks_per_row;
+  const uint64_t n_chunks = ROWS ? a.total_chunks : a.chunks_per_row;
+  // Row-strided shares: the row and column of the block's first chunk.
+  [[maybe_unused]] const uint64_t cpr = a.chunks_per_row;
+  [[maybe_unused]] const uint32_t row_b = ROWS ? static_cast<uint32_t>(__umul64hi(block_first, a.div_magic)) : 0u;
+  [[maybe_unused]] const uint32_t col_b = ROWS ? static_cast<uint32_t>(block_first - row_b * cpr) : 0u;
   // Share handled by this block (one share unless the all-to-all is
   // emulated on this GPU): uniform offsets into every rank's input.
   const uint32_t share = SHARES ? blockIdx.y : 0u;
-  const uint64_t x_off = (SHARES ? share * a.x_share_stride : 0) + (ROWS ? row * a.x_row_stride : 0);
-  const uint64_t s_off = (SHARES ? share * a.scale_share_stride : 0) + (ROWS ? row * a.scale_row_stride : 0);
+  const uint64_t x_off = SHARES ? share * a.x_share_stride : 0;
+  const uint64_t s_off = SHARES ? share * a.scale_share_stride : 0;
 
+  // Row-strided shares: chunk base + j*QRS_BLOCK sits at (row_b + dr,
+  // col[j]); col[j] is the chunk's index within its row.
+  [[maybe_unused]] uint32_t row_of[CH];
+  [[maybe_unused]] uint32_t col_of[CH];
   u32x4 xv[CH][W];
   float sv[CH][W];
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
     const uint64_t c = base + static_cast<uint64_t>(j) * QRS_BLOCK;
+    if constexpr (ROWS) {
+      const uint32_t t = col_b + threadIdx.x + j * QRS_BLOCK;
+      const uint32_t dr = (t * a.div_m20) >> 20;
+      row_of[j] = row_b + dr;
+      col_of[j] = t - dr * static_cast<uint32_t>(cpr);
+    }
     if (c < n_chunks) {
+      if constexpr (ROWS) {
+        // One byte offset per lane for all ranks' codes and one for their
+        // scales: a single 64-bit add per load.
+        const uint64_t xb = (static_cast<uint64_t>(row_of[j]) * a.x_row_stride + col_of[j]) * sizeof(u32x4);
+        // A scale slice spans less than 4 GiB (checked at launch): a 32-bit
+        // offset, which also keeps the compiler from redoing the row product
+        // for every rank.
+        const uint32_t sb = row_of[j] * a.scale_row_stride + static_cast<uint32_t>(scale_byte_offset<SL>(col_of[j]));
 #pragma unroll
-      for (int r = 0; r < W; ++r) xv[j][r] = load_stream(a.x[r] + x_off + c);
+        for (int r = 0; r < W; ++r)
+          xv[j][r] = load_stream(reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.x[r]) + xb));
 #pragma unroll
-      for (int r = 0; r < W; ++r) sv[j][r] = load_scale<SL>(static_cast<const char*>(a.scales[r]) + s_off, c);
+        for (int r = 0; r < W; ++r) sv[j][r] = load_scale_at<SL>(static_cast<const char*>(a.scales[r]) + sb);
+      } else if constexpr (OFF32) {
+        const uint32_t xb = static_cast<uint32_t>(c) * static_cast<uint32_t>(sizeof(u32x4));
+        const uint32_t sb = static_cast<uint32_t>(scale_byte_offset<SL>(c));
+#pragma unroll
+        for (int r = 0; r < W; ++r)
+          xv[j][r] = load_stream(reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.x[r]) + xb));
+#pragma unroll
+        for (int r = 0; r < W; ++r) sv[j][r] = load_scale_at<SL>(static_cast<const char*>(a.scales[r]) + sb);
+      } else {
+#pragma unroll
+        for (int r = 0; r < W; ++r) xv[j][r] = load_stream(a.x[r] + x_off + c);
+#pragma unroll
+        for (int r = 0; r < W; ++r) sv[j][r] = load_scale<SL>(static_cast<const char*>(a.scales[r]) + s_off, c);
+      }
     }
   }
 
-  u32x4* const out = static_cast<u32x4*>(a.out[share]) + (ROWS ? row * a.out_row_stride : 0);
+  u32x4* const out = static_cast<u32x4*>(a.out[share]);
   constexpr bool kStage = QRS_STAGE_STORES == 2 || (QRS_STAGE_STORES == 1 && OF == kOutF32);
   __shared__ u32x4 stage[kStage ? QRS_BLOCK * P : 1];
   [[maybe_unused]] const int lane = threadIdx.x & 63;
@@ -294,8 +358,16 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
       fold_chunk<W, XF>(xv[j], sv[j], acc);
       pack_chunk<OF>(acc, piece);
       if constexpr (!kStage) {
+        const uint64_t oc = ROWS ? static_cast<uint64_t>(row_of[j]) * a.out_row_stride + col_of[j] * P : c * P;
 #pragma unroll
-        for (int q = 0; q < P; ++q) store_stream(out + c * P + q, piece[q]);
+        for (int q = 0; q < P; ++q) {
+          if constexpr (OFF32)
+            store_stream(reinterpret_cast<u32x4*>(reinterpret_cast<char*>(out) +
+                                                  static_cast<uint32_t>(oc + q) * static_cast<uint32_t>(sizeof(u32x4))),
+                         piece[q]);
+          else
+            store_stream(out + oc + q, piece[q]);
+        }
       }
     }
     if constexpr (kStage) {
@@ -312,10 +384,34 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
       u32x4 staged[P];
 #pragma unroll
       for (int q = 0; q < P; ++q) staged[q] = wave_stage[q * 64 + lane];
+      // Row-strided shares: row and column of the wave's first chunk; a
+      // chunk d < 64 further on is at most one row later (a row has at
+      // least 64 chunks).
+      [[maybe_unused]] uint32_t wrow = 0;
+      [[maybe_unused]] uint32_t wcol = 0;
+      if constexpr (ROWS) {
+        const uint32_t t = col_b + (threadIdx.x & ~63) + j * QRS_BLOCK;
+        const uint32_t dr = (t * a.div_m20) >> 20;
+        wrow = row_b + dr;
+        wcol = t - dr * static_cast<uint32_t>(cpr);
+      }
 #pragma unroll
       for (int q = 0; q < P; ++q) {
         const int k = q * 64 + lane;  // piece k of the wave's range belongs to chunk k / P
-        if (wave_first_chunk + k / P < n_chunks) store_stream(out + wave_first_chunk * P + k, staged[q]);
+        if (wave_first_chunk + k / P < n_chunks) {
+          if constexpr (ROWS) {
+            uint32_t col = wcol + k / P;
+            const bool next = col >= static_cast<uint32_t>(cpr);
+            col = next ? col - static_cast<uint32_t>(cpr) : col;
+            const uint32_t orow = wrow + (next ? 1u : 0u);
+            store_stream(out + static_cast<uint64_t>(orow) * a.out_row_stride + col * P + k % P, staged[q]);
+          } else if constexpr (OFF32) {
+            const uint32_t ob = static_cast<uint32_t>(wave_first_chunk * P + k) * static_cast<uint32_t>(sizeof(u32x4));
+            store_stream(reinterpret_cast<u32x4*>(reinterpret_cast<char*>(out) + ob), staged[q]);
+          } else {
+            store_stream(out + wave_first_chunk * P + k, staged[q]);
+          }
+        }
       }
     }
   }
@@ -334,13 +430,30 @@ hipError_t launch_typed(const ReduceLaunch& l, hipStream_t stream) {
   if (l.n_shares != 1 && l.n_shares != W) return hipErrorInvalidValue;
   a.chunks_per_row = l.row_elems / kChunk;
   const uint64_t per_block = static_cast<uint64_t>(QRS_BLOCK) * QRS_CHUNKS_PER_LANE;
-  const uint64_t bpr = (a.chunks_per_row + per_block - 1) / per_block;
-  const uint64_t blocks = bpr * l.n_rows;
-  if (bpr > 0xFFFFFFFFull || blocks > 0x7FFFFFFFull || l.n_rows > 0xFFFFFFFFull) return hipErrorInvalidValue;
-  a.blocks_per_row = static_cast<uint32_t>(bpr);
-  a.x_row_stride = l.x_row_stride / 16;
-  a.scale_row_stride = l.scale_row_stride;
-  a.out_row_stride = l.out_row_stride / 16;
+  if (l.n_rows > (1ull << 40) / a.chunks_per_row) return hipErrorInvalidValue;
+  a.total_chunks = a.chunks_per_row * l.n_rows;
+  const uint64_t blocks = (a.total_chunks + per_block - 1) / per_block;
+  if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  // Row split constants. Exact when the chunk index is below 2^39 (block
+  // count above) and when a lane's offset from its block's first row start,
+  // below chunks_per_row + per_block, stays under 1024 with
+  // chunks_per_row < 1024: the rounding excess of each product then stays
+  // below 1 / chunks_per_row.
+  if (l.n_rows > 1 && (a.chunks_per_row < 64 || a.chunks_per_row + per_block > 1024)) return hipErrorInvalidValue;
+  a.div_magic = ~0ull / a.chunks_per_row + 1;
+  a.div_m20 = static_cast<uint32_t>(((1ull << 20) + a.chunks_per_row - 1) / a.chunks_per_row);
+  // Row-strided shares: rows and row strides below 2^32 (of their units),
+  // so each row offset is one 32 x 32 -> 64-bit multiply.
+  if (l.n_rows > 1 && (l.n_rows > 0xFFFFFFFFull || l.x_row_stride / 16 > 0xFFFFFFFFull ||
+                       l.scale_row_stride > 0xFFFFFFFFull || l.out_row_stride / 16 > 0xFFFFFFFFull))
+    return hipErrorInvalidValue;
+  // ... and each scale slice spans less than 4 GiB (32-bit offsets).
+  const uint64_t scale_row_bytes = l.row_elems / 32;  // both layouts: 1/32 byte per element
+  if (l.n_rows > 1 && (l.n_rows - 1) * l.scale_row_stride + scale_row_bytes > 0xFFFFFFFFull)
+    return hipErrorInvalidValue;
+  a.x_row_stride = static_cast<uint32_t>(l.x_row_stride / 16);
+  a.scale_row_stride = static_cast<uint32_t>(l.scale_row_stride);
+  a.out_row_stride = static_cast<uint32_t>(l.out_row_stride / 16);
   a.x_share_stride = l.x_share_stride / 16;
   a.scale_share_stride = l.scale_share_stride;
   const dim3 grid(static_cast<uint32_t>(blocks), l.n_shares);
@@ -349,6 +462,10 @@ hipError_t launch_typed(const ReduceLaunch& l, hipStream_t stream) {
     hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF, kAddrShares>), grid, dim3(QRS_BLOCK), 0, stream, a);
   } else if (l.n_rows > 1) {
     hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF, kAddrRows>), grid, dim3(QRS_BLOCK), 0, stream, a);
+  } else if (a.chunks_per_row * OutPieces<OF>::kCount * sizeof(u32x4) < (1ull << 32)) {
+    // The output is the largest of the share's tensors (at least 2 bytes per
+    // element against 1 + 1/32 for a slice and its scales).
+    hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF, kAddrFlat32>), grid, dim3(QRS_BLOCK), 0, stream, a);
   } else {
     hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF, kAddrFlat>), grid, dim3(QRS_BLOCK), 0, stream, a);
   }

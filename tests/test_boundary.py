@@ -301,3 +301,34 @@ def test_strided_run_rejects_address_overflow(fake_ptr_lib):
         qrs.Status.INVALID_ARG
     assert lib.qrs_run_strided(p.handle, xs, 1024, ss, 32, A + (4 << 30), 1 << 61, None, 0, None) == \
         qrs.Status.INVALID_ARG
+
+
+def test_strided_run_rejects_row_strides_of_4gib(fake_ptr_lib):
+    # Row offsets are 32 x 32-bit products in the kernel: each row stride must
+    # stay below 4 GiB (checked on the host, before any launch).
+    lib = fake_ptr_lib
+    p = qrs.plan(2, 4, 1024, "e4m3fn", "f32_group128", "f32")  # 2 rows
+    A = 1 << 44
+    xs = (ctypes.c_void_p * 2)(A, A + (8 << 30))
+    ss = (ctypes.c_void_p * 2)(A + (16 << 30), A + (24 << 30))
+    out = A + (32 << 30)
+
+    def call(ldx, lds, ldo):
+        return lib.qrs_run_strided(p.handle, xs, ldx, ss, lds, out, ldo, None, 0, None)
+
+    assert call(1 << 32, 8, 1024) == qrs.Status.INVALID_ARG  # x: 4 GiB
+    assert call(1024, 1 << 30, 1024) == qrs.Status.INVALID_ARG  # fp32 scales: 2^30 * 4 bytes
+    assert call(1024, 8, 1 << 30) == qrs.Status.INVALID_ARG  # fp32 out: 2^30 * 4 bytes
+    assert "4 GiB" in lib.qrs_last_error().decode()
+
+
+def test_strided_run_rejects_scale_span_of_4gib(fake_ptr_lib):
+    lib = fake_ptr_lib
+    p = qrs.plan(2, 2 * 5000, 1024, "e4m3fn", "f32_group128", "f32")  # 5000 rows
+    A = 1 << 44
+    xs = (ctypes.c_void_p * 2)(A, A + (64 << 30))
+    ss = (ctypes.c_void_p * 2)(A + (128 << 30), A + (192 << 30))
+    out = A + (256 << 30)
+    # 5000 rows of fp32 scales 2^18 elements (1 MiB) apart: 4.9 GiB span.
+    assert lib.qrs_run_strided(p.handle, xs, 1024, ss, 1 << 18, out, 1024, None, 0, None) == qrs.Status.INVALID_ARG
+    assert "4 GiB" in lib.qrs_last_error().decode()

@@ -79,3 +79,50 @@ def test_strided_rejects_mismatched_strides(gpu):
     out = torch.zeros(4, 1024, dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError):
         qrs.run_strided(p, [a[:, :1024], b[:, :1024]], s, out)
+
+
+@pytest.mark.parametrize("h,rows", [(1152, 61), (7168, 9), (5120, 13), (1024, 33)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_rows_crossing_waves_and_blocks(gpu, h, rows, out_dtype):
+    # Rows of H/16 chunks that are not a multiple of a wave's 64 chunks or a
+    # block's 256: waves and blocks start mid-row and span row ends.
+    _case(8, rows, h, "e5m2", "e8m0_block32", out_dtype, extra_cols=128, c0=128, seed=h + rows)
+    _case(2, rows, h, "int8", "f32_group128", out_dtype, extra_cols=256, c0=0, seed=h + rows + 1)
+
+
+@pytest.mark.parametrize("name", ["w8_bs65536_h5120_mx_e5m2_f32", "w8_bs8192_h7168_e5m2_bf16"])
+def test_full_size_row_interleaved_receive_buffer(gpu, name):
+    # The W slices interleaved by row in one [rows, W, H] buffer (and the
+    # scales in [rows, W, H/G]): every slice is a row-strided view. Sampled
+    # rows against the oracle, the whole output against qrs_run on the same
+    # values in contiguous slices.
+    wl = workloads.WORKLOADS[name]
+    xs, ss = workloads.generate(wl)
+    w, rows, h = wl.world_size, wl.rows, wl.h
+    bx = torch.empty((rows, w, h), dtype=torch.uint8, device="cuda")
+    bs = torch.empty((rows, w) + ss[0].shape[1:], dtype=torch.float32 if ss[0].dtype == np.float32 else torch.uint8,
+                     device="cuda")
+    for r in range(w):
+        bx[:, r, :].copy_(torch.from_numpy(xs[r]))
+        bs[:, r, :].copy_(torch.from_numpy(ss[r]))
+    p = qrs.plan(w, wl.bs, h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    out = torch.empty((rows, h), dtype=OUT_TORCH[wl.out_dtype], device="cuda")
+    qrs.run_strided(p, [bx[:, r, :] for r in range(w)], [bs[:, r, :] for r in range(w)], out)
+    torch.cuda.synchronize()
+    got = out_bits(out)
+    # The prepared launch (arguments marshalled once) gives the same bytes.
+    out3 = torch.empty_like(out)
+    qrs.StridedLaunch(p, [bx[:, r, :] for r in range(w)], [bs[:, r, :] for r in range(w)], out3)()
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), out3.view(torch.uint8))
+    sample = np.unique(np.concatenate([[0, 1, rows - 1], np.random.default_rng(5).integers(0, rows, 13)]))
+    want = oracle.reduce_scatter_share([x[sample] for x in xs], [s[sample] for s in ss], wl.x_format,
+                                       wl.scale_layout, wl.out_dtype)
+    assert_parity(got[sample], oracle_bits(want, wl.out_dtype), wl.out_dtype, name)
+    del bx, bs
+    dx = [torch.from_numpy(x).cuda() for x in xs]
+    ds = [torch.from_numpy(s).cuda() for s in ss]
+    out2 = torch.empty_like(out)
+    qrs.run(p, dx, ds, out2)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.uint8), out2.view(torch.uint8))
