@@ -39,3 +39,29 @@ def test_output_beyond_4gib(gpu, x_format, scale_layout):
     # The very last rows, on the host as well.
     tail = out[-blk:].cpu().view(torch.int32).numpy()
     assert np.array_equal(tail, want)
+
+
+def test_all_shares_inputs_beyond_4gib(gpu):
+    # Each rank's whole input (both shares' row blocks) is just over 4 GiB, so
+    # the launch takes the 64-bit-offset all-shares kernel. Every rank's input
+    # is one 64-row block repeated, so every share is the oracle's result for
+    # those blocks, repeated.
+    w, h, rows, blk = 2, 8192, 262208, 64  # w * rows * h = 4.296e9 > 2^32
+    wl = workloads.Workload("large_all", w, w * blk, h, "e4m3fn", "e8m0_block32", "bf16",
+                            x_dist="normal", x_param=40, scale_lo=110, scale_hi=140, seed=41)
+    xs, ss = workloads.generate(wl)  # one [64, H] block per rank
+    want = oracle.reduce_scatter_share(xs, ss, "e4m3fn", "e8m0_block32", "bf16")
+    log(f"[large] all shares: W={w}, each rank's input [{w * rows}, {h}] ({w * rows * h / 2**30:.2f} GiB)")
+    reps = w * rows // blk
+    dx = [torch.from_numpy(x).cuda().repeat(reps, 1) for x in xs]
+    ds = [torch.from_numpy(s).cuda().repeat(reps, 1) for s in ss]
+    assert dx[0].numel() > 2**32
+    outs = [torch.empty((rows, h), dtype=torch.bfloat16, device="cuda") for _ in range(w)]
+    p = qrs.plan(w, w * rows, h, "e4m3fn", "e8m0_block32", "bf16")
+    qrs.run_all_shares(p, dx, ds, outs)
+    torch.cuda.synchronize()
+    del dx, ds
+    want_t = torch.from_numpy(want.view(np.int16)).cuda()
+    for j, o in enumerate(outs):
+        got = o.view(torch.int16).view(rows // blk, blk, h)
+        assert torch.equal(got, want_t.unsqueeze(0).expand(rows // blk, blk, h)), f"share {j}"
