@@ -1,0 +1,70 @@
+"""bench.py's contract: one GPU only, the JSON line's fields, the traffic
+lookup that ties a counter summary to the kernel source it was taken on, and
+the CPU-oracle baseline."""
+
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+import workloads  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr
+    assert res.stdout == ""
+
+
+def test_traffic_is_read_only_for_the_source_it_was_taken_on(tmp_path, monkeypatch):
+    src_rel = bench.KERNEL_SOURCES["share"]
+    src = tmp_path / src_rel
+    src.parent.mkdir(parents=True)
+    src.write_bytes(b"kernel source v1")
+    (tmp_path / "profiles").mkdir()
+    summary = tmp_path / "profiles" / "traffic_reduce_w8_bs16384_h8192_mx_e4m3_bf16.txt"
+    digest = hashlib.sha256(b"kernel source v1").hexdigest()
+    summary.write_text(f"# header\nkernel_source_sha256: {digest}\nhbm_bytes_per_launch: 177272000\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.read_traffic("w8_bs16384_h8192_mx_e4m3_bf16", "share") == 177272000
+    assert bench.read_traffic("w8_bs65536_h5120_mx_e5m2_f32", "share") is None  # no summary
+    src.write_bytes(b"kernel source v2")  # the kernel changed since the counters were taken
+    assert bench.read_traffic("w8_bs16384_h8192_mx_e4m3_bf16", "share") is None
+
+
+def test_cpu_baseline_fields():
+    wl = workloads.WORKLOADS["w2_bs32_h1024_int8_f32"]
+    xs, ss = workloads.generate(wl)
+    cb = bench.cpu_baseline(wl, xs, ss, min_seconds=0.0, min_reps=3)
+    assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
+    assert cb["value"] > 0 and cb["unit"] == "GB/s" and cb["cores"] == 1 and cb["kind"] == "oracle"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("op", ["share", "strided", "all_shares", "quantize"])
+def test_json_line(gpu, op):
+    wl = "w4_bs4096_h4096_e4m3_bf16"
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--op", op, "--workload", wl, "--steps",
+                          "20", "--warmup", "10", "--no-cpu-baseline"], capture_output=True, text=True, timeout=240)
+    assert res.returncode == 0, res.stderr[-2000:]
+    lines = [ln for ln in res.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, "exactly one line on stdout"
+    d = json.loads(lines[0])
+    for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better", "scaling",
+              "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline"):
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["steps"] == 20 and d["warmup"] == 10
+    assert d["value"] > 0 and d["unit"] == "GB/s" and d["higher_is_better"] is True
+    assert d["vs_baseline"] is None and d["data"] == "synthetic" and d["cpu_baseline"] is None
+    assert d["config"]["workload"].startswith(wl) and d["config"]["op"] == op
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
+    assert "traffic" in r and 0 < r["frac"] < 1 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
