@@ -332,3 +332,43 @@ def test_strided_run_rejects_scale_span_of_4gib(fake_ptr_lib):
     # 5000 rows of fp32 scales 2^18 elements (1 MiB) apart: 4.9 GiB span.
     assert lib.qrs_run_strided(p.handle, xs, 1024, ss, 1 << 18, out, 1024, None, 0, None) == qrs.Status.INVALID_ARG
     assert "4 GiB" in lib.qrs_last_error().decode()
+
+
+def test_last_error_is_per_thread(lib):
+    # Two threads fail at the same time with different arguments; each then
+    # reads its own message, not the other thread's.
+    import threading
+
+    barrier = threading.Barrier(2)
+    seen = {}
+
+    def worker(name, w, h):
+        handle = ctypes.c_void_p()
+        ws = ctypes.c_size_t()
+        for _ in range(200):
+            st = lib.qrs_plan(w, 8 * w, h, 1, 1, 1, ctypes.byref(handle), ctypes.byref(ws))
+            barrier.wait()  # both calls have failed before either reads
+            msg = lib.qrs_last_error().decode()
+            barrier.wait()
+            if st != qrs.Status.INVALID_ARG or msg != seen.setdefault(name, msg):
+                seen[name] = f"changed: {msg}"
+                return
+
+    a = threading.Thread(target=worker, args=("w", 3, 1024))
+    b = threading.Thread(target=worker, args=("h", 2, 1000))
+    a.start()
+    b.start()
+    a.join(60)
+    b.join(60)
+    assert seen["w"].startswith("world_size 3"), seen
+    assert seen["h"].startswith("h 1000"), seen
+
+
+def test_last_error_cleared_by_a_successful_call(lib):
+    handle = ctypes.c_void_p()
+    ws = ctypes.c_size_t()
+    assert lib.qrs_plan(3, 24, 1024, 1, 1, 1, ctypes.byref(handle), ctypes.byref(ws)) == qrs.Status.INVALID_ARG
+    assert lib.qrs_last_error().decode() != ""
+    assert lib.qrs_plan(2, 16, 1024, 1, 1, 1, ctypes.byref(handle), ctypes.byref(ws)) == qrs.Status.OK
+    assert lib.qrs_last_error().decode() == ""
+    lib.qrs_plan_destroy(handle)

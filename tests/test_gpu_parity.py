@@ -160,6 +160,29 @@ def test_runs_on_the_given_stream(gpu):
     assert_parity(out_bits(out), want, wl.out_dtype, "stream order")
 
 
+def test_one_plan_on_two_streams_at_once(gpu):
+    """A plan is immutable: launches of one plan interleaved on two streams,
+    with different inputs, each give their own oracle result."""
+    import quantized_collective_reduction_amd as qrs
+
+    wl = workloads.WORKLOADS["w8_bs8192_h7168_e5m2_bf16"].with_(bs=8 * 96)
+    cases = [workloads.generate(wl), workloads.generate(wl.with_(seed=9))]
+    p = qrs.plan(8, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    dev_in = [to_device(xs, ss) for xs, ss in cases]
+    outs = [[empty_out(wl.rows, wl.h, wl.out_dtype).fill_(float("nan")) for _ in range(4)] for _ in cases]
+    torch.cuda.synchronize()
+    for i in range(4):
+        for k in range(2):
+            qrs.run(p, dev_in[k][0], dev_in[k][1], outs[k][i], stream=streams[k])
+    torch.cuda.synchronize()
+    for k, (xs, ss) in enumerate(cases):
+        want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype),
+                           wl.out_dtype)
+        for i in range(4):
+            assert_parity(out_bits(outs[k][i]), want, wl.out_dtype, f"stream {k} launch {i}")
+
+
 def test_misaligned_device_pointers_rejected(gpu):
     import quantized_collective_reduction_amd as qrs
 
