@@ -63,6 +63,13 @@
 #ifndef QRS_XCD_REMAP
 #define QRS_XCD_REMAP 0
 #endif
+// MX modes: where to decode and scale with the gfx950 scaled fp8 conversions
+// (one instruction per two products) instead of decode, then multiply.
+// 0: never; 1: fp32 outputs only (measured 0.6-0.7 % faster there, and 1.5-2 %
+// slower with 16-bit outputs); 2: always.
+#ifndef QRS_MX_SCALED_CVT
+#define QRS_MX_SCALED_CVT 1
+#endif
 // 1: block barrier around the LDS exchange; 0: wave-local ordering only.
 #ifndef QRS_STAGE_BLOCK_SYNC
 #define QRS_STAGE_BLOCK_SYNC 0
@@ -130,14 +137,31 @@ __device__ __forceinline__ float decode_e8m0(uint32_t b) {
   return __builtin_bit_cast(float, bits);
 }
 
-template <int SL>
+// Whether a kernel instantiation uses the scaled conversions (MX scales,
+// output type per QRS_MX_SCALED_CVT).
+template <int SL, int OF>
+constexpr bool kScaledCvt =
+    SL == kScaleE8M0Block32 && (QRS_MX_SCALED_CVT == 2 || (QRS_MX_SCALED_CVT == 1 && OF == kOutF32));
+
+// The scale operand of an MX chunk. For the scaled conversions (below) it is
+// the E8M0 byte placed in an fp32 exponent field, which is the form those
+// instructions read; otherwise the decoded scale.
+template <bool SCALED>
+__device__ __forceinline__ float mx_scale_operand(uint32_t b) {
+  if constexpr (SCALED)
+    return __builtin_bit_cast(float, b << 23);
+  else
+    return decode_e8m0(b);
+}
+
+template <int SL, bool SCALED>
 __device__ __forceinline__ float load_scale(const void* base, uint64_t chunk) {
   if constexpr (SL == kScaleF32Group128) {
     // 128 elements = 8 chunks share one fp32 scale.
     return static_cast<const float*>(base)[chunk >> 3];
   } else {
     // 32 elements = 2 chunks share one E8M0 byte.
-    return decode_e8m0(static_cast<const uint8_t*>(base)[chunk >> 1]);
+    return mx_scale_operand<SCALED>(static_cast<const uint8_t*>(base)[chunk >> 1]);
   }
 }
 
@@ -147,13 +171,31 @@ __device__ __forceinline__ uint64_t scale_byte_offset(uint64_t chunk) {
   return SL == kScaleF32Group128 ? (chunk >> 3) * sizeof(float) : (chunk >> 1);
 }
 
-template <int SL>
+template <int SL, bool SCALED>
 __device__ __forceinline__ float load_scale_at(const char* p) {
   if constexpr (SL == kScaleF32Group128) {
     return *reinterpret_cast<const float*>(p);
   } else {
-    return decode_e8m0(*reinterpret_cast<const uint8_t*>(p));
+    return mx_scale_operand<SCALED>(*reinterpret_cast<const uint8_t*>(p));
   }
+}
+
+// The products p = fp32(x * scale) of two adjacent codes of a 32-bit word
+// (bytes 0,1 or 2,3) in MX mode (E8M0 scales, fp8 codes): gfx950's scaled
+// conversions v_cvt_scalef32_pk_f32_fp8 / _bf8 decode and multiply by
+// 2^(E8M0 - 127) in one instruction. An fp8 value times a power of two in
+// [2^-127, 2^127] never needs rounding in binary32 (its lowest set bit stays
+// at or above 2^-143), so the exact result is the IEEE product; on the
+// device these instructions give that product, bit for bit, for every code
+// and every E8M0 byte (2^-127 for byte 0, NaN for 255, overflow to
+// infinity), which the GPU code-probe tests check.
+template <int XF, bool SCALED>
+__device__ __forceinline__ f32x2 product_pair(uint32_t w, float s, bool hi) {
+  static_assert(SCALED && XF != kXInt8, "scaled conversions: MX scales with fp8 codes only");
+  if constexpr (XF == kXE4M3FN)
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, s, true) : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, s, false);
+  else
+    return hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w, s, true) : __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(w, s, false);
 }
 
 struct KernelArgs {
@@ -192,35 +234,60 @@ __device__ __forceinline__ void stage_sync() {
 }
 
 // acc[0..15] = rank-ordered fold of the dequantized products of one chunk.
-template <int W, int XF>
+template <int W, int XF, bool SCALED>
 __device__ __forceinline__ void fold_chunk(const u32x4 (&xv)[W], const float (&sv)[W], float (&acc)[kChunk]) {
-  // Rank 0 starts the fold: acc = p_0.
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t w = xv[0][q];
-    const f32x2 lo = decode_pair<XF>(w, false);
-    const f32x2 hi = decode_pair<XF>(w, true);
-    acc[4 * q + 0] = lo.x * sv[0];
-    acc[4 * q + 1] = lo.y * sv[0];
-    acc[4 * q + 2] = hi.x * sv[0];
-    acc[4 * q + 3] = hi.y * sv[0];
-  }
-  // Ranks 1..W-1 in order: acc = acc + p_r, each a separate rounding.
-#pragma unroll
-  for (int r = 1; r < W; ++r) {
+  if constexpr (SCALED) {
+    // Rank 0 starts the fold: acc = p_0.
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t w = xv[r][q];
+      const f32x2 lo = product_pair<XF, true>(xv[0][q], sv[0], false);
+      const f32x2 hi = product_pair<XF, true>(xv[0][q], sv[0], true);
+      acc[4 * q + 0] = lo.x;
+      acc[4 * q + 1] = lo.y;
+      acc[4 * q + 2] = hi.x;
+      acc[4 * q + 3] = hi.y;
+    }
+    // Ranks 1..W-1 in order: acc = acc + p_r, each a separate rounding.
+#pragma unroll
+    for (int r = 1; r < W; ++r) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x2 lo = product_pair<XF, true>(xv[r][q], sv[r], false);
+        const f32x2 hi = product_pair<XF, true>(xv[r][q], sv[r], true);
+        acc[4 * q + 0] = acc[4 * q + 0] + lo.x;
+        acc[4 * q + 1] = acc[4 * q + 1] + lo.y;
+        acc[4 * q + 2] = acc[4 * q + 2] + hi.x;
+        acc[4 * q + 3] = acc[4 * q + 3] + hi.y;
+      }
+    }
+  } else {
+    // The same fold with the decode and the rounded multiply written out.
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = xv[0][q];
       const f32x2 lo = decode_pair<XF>(w, false);
       const f32x2 hi = decode_pair<XF>(w, true);
-      const float p0 = lo.x * sv[r];
-      const float p1 = lo.y * sv[r];
-      const float p2 = hi.x * sv[r];
-      const float p3 = hi.y * sv[r];
-      acc[4 * q + 0] = acc[4 * q + 0] + p0;
-      acc[4 * q + 1] = acc[4 * q + 1] + p1;
-      acc[4 * q + 2] = acc[4 * q + 2] + p2;
-      acc[4 * q + 3] = acc[4 * q + 3] + p3;
+      acc[4 * q + 0] = lo.x * sv[0];
+      acc[4 * q + 1] = lo.y * sv[0];
+      acc[4 * q + 2] = hi.x * sv[0];
+      acc[4 * q + 3] = hi.y * sv[0];
+    }
+#pragma unroll
+    for (int r = 1; r < W; ++r) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = xv[r][q];
+        const f32x2 lo = decode_pair<XF>(w, false);
+        const f32x2 hi = decode_pair<XF>(w, true);
+        const float p0 = lo.x * sv[r];
+        const float p1 = lo.y * sv[r];
+        const float p2 = hi.x * sv[r];
+        const float p3 = hi.y * sv[r];
+        acc[4 * q + 0] = acc[4 * q + 0] + p0;
+        acc[4 * q + 1] = acc[4 * q + 1] + p1;
+        acc[4 * q + 2] = acc[4 * q + 2] + p2;
+        acc[4 * q + 3] = acc[4 * q + 3] + p3;
+      }
     }
   }
 }
@@ -273,6 +340,7 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
   constexpr bool ROWS = ADDR == kAddrRows;
   constexpr bool SHARES = ADDR == kAddrShares;
   constexpr bool OFF32 = ADDR == kAddrFlat32;
+  constexpr bool SCALED = kScaledCvt<SL, OF>;
   constexpr int CH = QRS_CHUNKS_PER_LANE;
   constexpr int P = OutPieces<OF>::kCount;
   static_assert(!ROWS || CH <= 2, "row split assumes a lane's offset from its block's first chunk < 1024");
@@ -325,7 +393,7 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
         for (int r = 0; r < W; ++r)
           xv[j][r] = load_stream(reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.x[r]) + xb));
 #pragma unroll
-        for (int r = 0; r < W; ++r) sv[j][r] = load_scale_at<SL>(static_cast<const char*>(a.scales[r]) + sb);
+        for (int r = 0; r < W; ++r) sv[j][r] = load_scale_at<SL, SCALED>(static_cast<const char*>(a.scales[r]) + sb);
       } else if constexpr (OFF32) {
         const uint32_t xb = static_cast<uint32_t>(c) * static_cast<uint32_t>(sizeof(u32x4));
         const uint32_t sb = static_cast<uint32_t>(scale_byte_offset<SL>(c));
@@ -333,12 +401,12 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
         for (int r = 0; r < W; ++r)
           xv[j][r] = load_stream(reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.x[r]) + xb));
 #pragma unroll
-        for (int r = 0; r < W; ++r) sv[j][r] = load_scale_at<SL>(static_cast<const char*>(a.scales[r]) + sb);
+        for (int r = 0; r < W; ++r) sv[j][r] = load_scale_at<SL, SCALED>(static_cast<const char*>(a.scales[r]) + sb);
       } else {
 #pragma unroll
         for (int r = 0; r < W; ++r) xv[j][r] = load_stream(a.x[r] + x_off + c);
 #pragma unroll
-        for (int r = 0; r < W; ++r) sv[j][r] = load_scale<SL>(static_cast<const char*>(a.scales[r]) + s_off, c);
+        for (int r = 0; r < W; ++r) sv[j][r] = load_scale<SL, SCALED>(static_cast<const char*>(a.scales[r]) + s_off, c);
       }
     }
   }
@@ -355,7 +423,7 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
     u32x4 piece[P];
     if (c < n_chunks) {
       float acc[kChunk];
-      fold_chunk<W, XF>(xv[j], sv[j], acc);
+      fold_chunk<W, XF, SCALED>(xv[j], sv[j], acc);
       pack_chunk<OF>(acc, piece);
       if constexpr (!kStage) {
         const uint64_t oc = ROWS ? static_cast<uint64_t>(row_of[j]) * a.out_row_stride + col_of[j] * P : c * P;
