@@ -47,6 +47,11 @@ struct ReduceLaunch {
   void* out[kMaxWorld];
 };
 
+// Returns hipErrorInvalidValue, launching nothing, for shapes outside the
+// kernels' index ranges: more than 2^40 chunks of 16 elements in a share;
+// for n_rows > 1 also rows or a row stride (in its units) of 2^32 or more,
+// a scale slice spanning 4 GiB or more, or a row of fewer than 64 or more
+// than 768 chunks.
 hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream);
 
 // Producer-side quantization of n_elems bf16 values (a multiple of 128,
