@@ -48,7 +48,7 @@ struct ReduceLaunch {
 };
 
 // Returns hipErrorInvalidValue, launching nothing, for shapes outside the
-// kernels' index ranges: more than 2^40 chunks of 16 elements in a share;
+// kernels' index ranges: 2^39 or more chunks of 16 elements in a share;
 // for n_rows > 1 also rows or a row stride (in its units) of 2^32 or more,
 // a scale slice spanning 4 GiB or more, or a row of fewer than 64 or more
 // than 768 chunks.
