@@ -239,14 +239,17 @@ qrs_status qrs_plan_shape(qrs_plan_t plan, int64_t* rows_out, int64_t* h_out);
 /*
  * Recommended placement when the W rank slices of x (and of the scales)
  * share one allocation, for example the receive buffer of the all-to-all:
- * slice r at byte offset r * x_pitch (scales: r * scale_pitch). Slices
- * placed exactly rows*H bytes apart put the same offset of every slice in
- * the same HBM bank group, and the W concurrent read streams then evict each
- * other's DRAM rows; staggering consecutive slices by a bit over 1 MiB
- * avoids it (measured on MI355X with 16 MiB slices: 31.5 us back to back,
- * 28.9 us staggered). Any placement gives the same results; this only
- * affects speed. Offsets are multiples of 64 KiB (x) and 4 KiB (scales), so
- * alignment requirements hold.
+ * slice r at byte offset r * x_pitch (scales: r * scale_pitch). What the
+ * W concurrent read streams see of each other is the pitch modulo 4 MiB:
+ * near a multiple of 4 MiB the same offset of every slice falls in the same
+ * HBM bank group and the streams evict each other's DRAM rows (measured on
+ * MI355X: 16 MiB slices back to back 31.5 us, staggered 28.9 us; 7 MiB
+ * slices at a pitch of 0.25 MiB modulo 4 MiB 14.75 us, at 1.25 MiB 13.95
+ * us). The x pitch is the slice size rounded up to 64 KiB, plus the
+ * smallest stagger that makes it 1.25 MiB modulo 4 MiB; the scale pitch is
+ * the scale slice rounded up to 4 KiB plus 40 KiB. Any placement gives the
+ * same results; this only affects speed. Offsets are multiples of 64 KiB
+ * (x) and 4 KiB (scales), so alignment requirements hold.
  *
  *   x_pitch_out, scale_pitch_out  receive the pitches in bytes; either may be
  *                                 NULL.

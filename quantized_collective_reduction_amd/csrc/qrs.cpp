@@ -140,10 +140,13 @@ qrs_status qrs_slice_pitch(qrs_plan_t plan, int full_inputs, size_t* x_pitch_out
   const uint64_t rows = static_cast<uint64_t>(full_inputs ? plan->bs : plan->rows);
   const uint64_t x_bytes = rows * static_cast<uint64_t>(plan->h);
   const uint64_t s_bytes = plan->scale_layout == qrs::kScaleF32Group128 ? x_bytes / 128 * 4 : x_bytes / 32;
-  // Round up to the alignment unit, then add a stagger of 1.25 MiB (x) and
-  // 40 KiB (scales, 1/32 of the x stagger).
+  // x: round up to 64 KiB, then stagger to 1.25 MiB modulo 4 MiB (the
+  // residue the W read streams are fastest at, whatever the slice size).
+  // Scales: round up to 4 KiB, then a 40 KiB stagger.
   auto round_up = [](uint64_t v, uint64_t a) { return (v + a - 1) / a * a; };
-  if (x_pitch_out) *x_pitch_out = round_up(x_bytes, 64 * 1024) + 1280 * 1024;
+  const uint64_t period = uint64_t{4} << 20, residue = uint64_t{1280} << 10;
+  const uint64_t x_base = round_up(x_bytes, 64 * 1024);
+  if (x_pitch_out) *x_pitch_out = x_base + (residue + period - x_base % period) % period;
   if (scale_pitch_out) *scale_pitch_out = round_up(s_bytes, 4096) + 40 * 1024;
   return ok();
 }

@@ -213,7 +213,16 @@ def test_slice_pitch(lib):
     assert xp == 16384 * 8192 + 1280 * 1024
     p2 = qrs.plan(2, 6, 1152, "int8", "f32_group128", "f32")  # 3 rows: 3456 bytes per slice
     xp, sp = qrs.slice_pitch(p2)
-    assert xp == 65536 + 1280 * 1024 and xp % 65536 == 0 and sp == 4096 + 40 * 1024
+    assert xp == 1280 * 1024 and sp == 4096 + 40 * 1024  # 64 KiB, then staggered to 1.25 MiB
+    # Slices that are not a multiple of 4 MiB get the stagger that makes the
+    # pitch 1.25 MiB modulo 4 MiB: 7 MiB slices -> 9.25 MiB, 15 MiB -> 17.25.
+    p3 = qrs.plan(8, 8192, 7168, "e5m2", "f32_group128", "bf16")
+    assert qrs.slice_pitch(p3)[0] == (9 << 20) + (1 << 18)
+    p4 = qrs.plan(8, 24576, 5120, "e5m2", "e8m0_block32", "f32")
+    assert qrs.slice_pitch(p4)[0] == (17 << 20) + (1 << 18)
+    for bs, h in [(8, 1024), (16384, 1152), (65536, 5120), (12345 * 8, 1024)]:
+        xp = qrs.slice_pitch(qrs.plan(8, bs, h, "e4m3fn", "e8m0_block32", "bf16"))[0]
+        assert xp >= bs // 8 * h and xp % 65536 == 0 and xp % (4 << 20) == 1280 * 1024
     assert lib.qrs_slice_pitch(None, 0, None, None) == qrs.Status.INVALID_ARG
     assert lib.qrs_slice_pitch(p.handle, 2, None, None) == qrs.Status.INVALID_ARG
 
