@@ -244,7 +244,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU's share on one GPU only: run it with --gpus 1 "
-              "(the all-to-all between GPUs is not part of this build)", file=sys.stderr)
+              "(the all-to-all between GPUs is outside this library)", file=sys.stderr)
         sys.exit(2)
     if args.steps <= 0 or args.warmup < 0:
         sys.exit("--steps must be positive and --warmup non-negative")
