@@ -32,6 +32,13 @@
 // The definition has one rounding per product and per sum: never fuse.
 #pragma clang fp contract(off)
 
+// 16-bit outputs: where to pair each lane's two 16-byte pieces across the
+// wave's halves (v_permlane32_swap) so that each store instruction writes
+// one contiguous 1 KiB. 0: never; 1: with fp32 group scales only (measured
+// faster there, slower in the MX modes); 2: always.
+#ifndef QRS_SWAP_STORES
+#define QRS_SWAP_STORES 1
+#endif
 #ifndef QRS_BLOCK
 #define QRS_BLOCK 256
 #endif
@@ -341,6 +348,11 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
   constexpr bool SHARES = ADDR == kAddrShares;
   constexpr bool OFF32 = ADDR == kAddrFlat32;
   constexpr bool SCALED = kScaledCvt<SL, OF>;
+  constexpr bool kStage = QRS_STAGE_STORES == 2 || (QRS_STAGE_STORES == 1 && OF == kOutF32);
+  // Swapped stores need the whole wave active up to the stores: lanes past
+  // the end then load the last chunk again and store nothing.
+  constexpr bool kSwap = (QRS_SWAP_STORES == 2 || (QRS_SWAP_STORES == 1 && SL == kScaleF32Group128)) &&
+                         !kStage && !ROWS && OutPieces<OF>::kCount == 2;
   constexpr int CH = QRS_CHUNKS_PER_LANE;
   constexpr int P = OutPieces<OF>::kCount;
   static_assert(!ROWS || CH <= 2, "row split assumes a lane's offset from its block's first chunk < 1024");
@@ -373,14 +385,15 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
   float sv[CH][W];
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
-    const uint64_t c = base + static_cast<uint64_t>(j) * QRS_BLOCK;
+    const uint64_t c_lane = base + static_cast<uint64_t>(j) * QRS_BLOCK;
+    const uint64_t c = (kSwap && c_lane >= n_chunks) ? n_chunks - 1 : c_lane;
     if constexpr (ROWS) {
       const uint32_t t = col_b + threadIdx.x + j * QRS_BLOCK;
       const uint32_t dr = (t * a.div_m20) >> 20;
       row_of[j] = row_b + dr;
       col_of[j] = t - dr * static_cast<uint32_t>(cpr);
     }
-    if (c < n_chunks) {
+    if (kSwap || c < n_chunks) {
       if constexpr (ROWS) {
         // One byte offset per lane for all ranks' codes and one for their
         // scales: a single 64-bit add per load.
@@ -412,7 +425,6 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
   }
 
   u32x4* const out = static_cast<u32x4*>(a.out[share]);
-  constexpr bool kStage = QRS_STAGE_STORES == 2 || (QRS_STAGE_STORES == 1 && OF == kOutF32);
   __shared__ u32x4 stage[kStage ? QRS_BLOCK * P : 1];
   [[maybe_unused]] const int lane = threadIdx.x & 63;
   [[maybe_unused]] u32x4* const wave_stage = stage + (kStage ? (threadIdx.x & ~63) * P : 0);
@@ -421,7 +433,12 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
   for (int j = 0; j < CH; ++j) {
     const uint64_t c = base + static_cast<uint64_t>(j) * QRS_BLOCK;
     u32x4 piece[P];
-    if (c < n_chunks) {
+    if constexpr (kSwap) {
+      float acc[kChunk];
+      fold_chunk<W, XF, SCALED>(xv[j], sv[j], acc);
+      pack_chunk<OF>(acc, piece);
+    }
+    if (!kSwap && c < n_chunks) {
       float acc[kChunk];
       fold_chunk<W, XF, SCALED>(xv[j], sv[j], acc);
       pack_chunk<OF>(acc, piece);
@@ -436,6 +453,41 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
           else
             store_stream(out + oc + q, piece[q]);
         }
+      }
+    }
+    if constexpr (kSwap) {
+      // Lane l holds pieces 2l and 2l+1 of the wave's 128 (its chunk's two
+      // halves). Swap the lower half-wave's second pieces with the upper
+      // half-wave's first pieces: lane l < 32 then holds pieces 2l and
+      // 2l+64, lane l >= 32 pieces 2l-63 and 2l+1, so the first store writes
+      // pieces 0..63 and the second 64..127, each one contiguous 1 KiB.
+      u32x4 lo = piece[0], hi = piece[1];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const auto r = __builtin_amdgcn_permlane32_swap(lo[d], hi[d], false, false);
+        lo[d] = r[0];
+        hi[d] = r[1];
+      }
+      const uint32_t lane_id = threadIdx.x & 63u;
+      const uint64_t wave_first_chunk = block_first + static_cast<uint64_t>(j) * QRS_BLOCK + (threadIdx.x & ~63u);
+      const uint32_t p_lo = lane_id < 32u ? 2u * lane_id : 2u * lane_id - 63u;
+      const uint32_t p_hi = lane_id < 32u ? 2u * lane_id + 64u : 2u * lane_id + 1u;
+      // Piece p belongs to chunk wave_first_chunk + p / 2.
+      if (wave_first_chunk + p_lo / 2u < n_chunks) {
+        if constexpr (OFF32)
+          store_stream(reinterpret_cast<u32x4*>(reinterpret_cast<char*>(out) +
+                                                static_cast<uint32_t>(wave_first_chunk * 2 + p_lo) * 16u),
+                       lo);
+        else
+          store_stream(out + wave_first_chunk * 2 + p_lo, lo);
+      }
+      if (wave_first_chunk + p_hi / 2u < n_chunks) {
+        if constexpr (OFF32)
+          store_stream(reinterpret_cast<u32x4*>(reinterpret_cast<char*>(out) +
+                                                static_cast<uint32_t>(wave_first_chunk * 2 + p_hi) * 16u),
+                       hi);
+        else
+          store_stream(out + wave_first_chunk * 2 + p_hi, hi);
       }
     }
     if constexpr (kStage) {

@@ -65,3 +65,27 @@ def test_all_shares_inputs_beyond_4gib(gpu):
     for j, o in enumerate(outs):
         got = o.view(torch.int16).view(rows // blk, blk, h)
         assert torch.equal(got, want_t.unsqueeze(0).expand(rows // blk, blk, h)), f"share {j}"
+
+
+def test_bf16_output_beyond_4gib(gpu):
+    # A 16-bit output past 4 GiB takes the 64-bit-offset flat kernel; with
+    # fp32 group scales that kernel pairs pieces across the wave's halves
+    # before storing. One 64-row block repeated, checked as above.
+    w, h, rows, blk = 2, 8192, 262208, 64  # output rows * h * 2 bytes = 4.0005 GiB
+    wl = workloads.Workload("large16", w, w * blk, h, "int8", "f32_group128", "bf16",
+                            x_dist="int_uniform", x_param=127, scale_lo=-8, scale_hi=0, seed=37)
+    xs, ss = workloads.generate(wl)
+    want = oracle.reduce_scatter_share(xs, ss, "int8", "f32_group128", "bf16").view(np.int16)
+    log(f"[large] int8/f32_group128 -> bf16: {rows} x {h} ({rows * h * 2 / 2**30:.3f} GiB output)")
+    reps = rows // blk
+    dx = [torch.from_numpy(x).cuda().repeat(reps, 1) for x in xs]
+    ds = [torch.from_numpy(s).cuda().repeat(reps, 1) for s in ss]
+    out = torch.empty((rows, h), dtype=torch.bfloat16, device="cuda")
+    assert out.numel() * 2 > 2**32
+    p = qrs.plan(w, w * rows, h, "int8", "f32_group128", "bf16")
+    qrs.run(p, dx, ds, out)
+    torch.cuda.synchronize()
+    del dx, ds
+    want_t = torch.from_numpy(want).cuda()
+    got = out.view(torch.int16).view(reps, blk, h)
+    assert torch.equal(got, want_t.unsqueeze(0).expand(reps, blk, h))
