@@ -150,7 +150,11 @@ qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* con
  *
  *     out_shares[j] = Reduce_r( scales_r[block j] * x_r[block j] )
  *
- * with the same arithmetic as qrs_run. One launch covers all W shares.
+ * with the same arithmetic as qrs_run. Up to about 300 MB of algorithmic
+ * bytes per share one launch covers all W shares; larger shares are
+ * enqueued as W launches, one per share, on the same stream (measured
+ * faster on MI355X at those sizes). Either way the call only enqueues work,
+ * and the results are the same.
  *
  *   x_full        HOST array of W DEVICE pointers; x_full[r] is rank r's
  *                 uint8 codes [BS, H], contiguous, 16-byte aligned.

@@ -76,3 +76,29 @@ def test_all_shares_rejects_overlapping_outputs(gpu):
     with pytest.raises(qrs.QrsError) as ei:
         qrs.run_all_shares(p, xs, ss, outs)
     assert ei.value.status == qrs.Status.INVALID_ARG
+
+
+def test_all_shares_large_shares_one_launch_each(gpu):
+    """Shares of more than about 300 MB are enqueued one launch per share:
+    W=2, BS=32768, H=8192 MX E4M3FN -> bf16 is 545 MB per share. Both shares
+    checked on 24 sampled rows, all columns; the result must equal the same
+    inputs' shares computed by qrs_run on each row block."""
+    wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(world_size=2, bs=32768)
+    assert wl.algorithmic_bytes() > 300_000_000  # per share
+    log("[all_shares] generating 2 x [32768, 8192] inputs")
+    xs, ss = workloads.generate_full(wl)
+    got = _run(wl, xs, ss)
+    rng = np.random.default_rng(8)
+    rows = np.sort(np.concatenate([[0, wl.rows - 1], rng.choice(wl.rows, 22, replace=False)]))
+    for j, (rx, rs) in enumerate(oracle.all_to_all(xs, ss)):
+        want = oracle.reduce_scatter_share([x[rows] for x in rx], [s[rows] for s in rs],
+                                           wl.x_format, wl.scale_layout, wl.out_dtype)
+        assert_parity(got[j][rows], oracle_bits(want, wl.out_dtype), wl.out_dtype, f"share {j}")
+    p = qrs.plan(wl.world_size, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    for j, (rx, rs) in enumerate(oracle.all_to_all(xs, ss)):
+        dx = [torch.from_numpy(np.ascontiguousarray(x)).cuda() for x in rx]
+        ds = [torch.from_numpy(np.ascontiguousarray(s)).cuda() for s in rs]
+        out = empty_out(wl.rows, wl.h, wl.out_dtype)
+        qrs.run(p, dx, ds, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out_bits(out), got[j]), f"share {j}"

@@ -42,10 +42,11 @@ def test_output_beyond_4gib(gpu, x_format, scale_layout):
 
 
 def test_all_shares_inputs_beyond_4gib(gpu):
-    # Each rank's whole input (both shares' row blocks) is just over 4 GiB, so
-    # the launch takes the 64-bit-offset all-shares kernel. Every rank's input
-    # is one 64-row block repeated, so every share is the oracle's result for
-    # those blocks, repeated.
+    # Each rank's whole input (both shares' row blocks) is just over 4 GiB and
+    # each share's output too, so the shares run as one launch each (large
+    # shares) on the 64-bit-offset kernel, at row-block offsets past 2^32.
+    # Every rank's input is one 64-row block repeated, so every share is the
+    # oracle's result for those blocks, repeated.
     w, h, rows, blk = 2, 8192, 262208, 64  # w * rows * h = 4.296e9 > 2^32
     wl = workloads.Workload("large_all", w, w * blk, h, "e4m3fn", "e8m0_block32", "bf16",
                             x_dist="normal", x_param=40, scale_lo=110, scale_hi=140, seed=41)
