@@ -8,7 +8,7 @@
 //
 //   p_r = fp32(decode(x_r) * decode(scale_r))      one rounding
 //   acc = p_0, then acc = fp32(acc + p_r) for r = 1 .. W-1, in rank order
-//   out = acc (fp32) or round-to-nearest-even(acc) (bf16)
+//   out = acc (fp32) or round-to-nearest-even(acc) (bf16, fp16)
 //
 // Modes (same page, Constraints): FP8 E4M3FN / E5M2 x with one E8M0 scale per
 // 32 elements (MX), or INT8 / E4M3FN / E5M2 x with one fp32 scale per token
@@ -20,9 +20,13 @@
 // the codes plus one scale load per rank, decodes with the CDNA4 fp8/bf8
 // conversion instructions (two elements per instruction), multiplies and
 // adds in separate fp32 instructions (no contraction, so results match the
-// definition bit for bit), converts with the packed bf16 round-to-nearest-
-// even instruction, and writes 16-byte stores. All W loads are issued before
-// any arithmetic, so each lane has W*16 bytes in flight.
+// definition bit for bit), converts with the packed round-to-nearest-even
+// instructions, and writes 16-byte stores. MX modes with fp32 output decode
+// and scale in one scaled conversion instead (exact, see product_pair).
+// fp32 outputs go through LDS and 16-bit outputs with fp32 group scales
+// through a cross-half lane swap, so that each store instruction writes one
+// contiguous 1 KiB. Which variant each mode uses was chosen by measurement;
+// the macros below select them.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -32,13 +36,7 @@
 // The definition has one rounding per product and per sum: never fuse.
 #pragma clang fp contract(off)
 
-// 16-bit outputs: where to pair each lane's two 16-byte pieces across the
-// wave's halves (v_permlane32_swap) so that each store instruction writes
-// one contiguous 1 KiB. 0: never; 1: with fp32 group scales only (measured
-// faster there, slower in the MX modes); 2: always.
-#ifndef QRS_SWAP_STORES
-#define QRS_SWAP_STORES 1
-#endif
+// Threads per block.
 #ifndef QRS_BLOCK
 #define QRS_BLOCK 256
 #endif
@@ -62,6 +60,13 @@
 // 0: never stage, 1: stage fp32 output only, 2: always stage.
 #ifndef QRS_STAGE_STORES
 #define QRS_STAGE_STORES 1
+#endif
+// 16-bit outputs: where to pair each lane's two 16-byte pieces across the
+// wave's halves (v_permlane32_swap) so that each store instruction writes
+// one contiguous 1 KiB. 0: never; 1: with fp32 group scales only (measured
+// faster there, slower in the MX modes); 2: always.
+#ifndef QRS_SWAP_STORES
+#define QRS_SWAP_STORES 1
 #endif
 // Block-to-XCD placement: the hardware hands consecutive block ids to the
 // 8 XCDs in turn. With 1, block id b is renumbered so that XCD b % 8 walks
