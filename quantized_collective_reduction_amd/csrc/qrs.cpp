@@ -62,7 +62,10 @@ qrs_status check_mode(qrs_x_dtype x_dtype, qrs_scale_layout scale_layout) {
 
 // Per-share algorithmic bytes above which qrs_run_all_shares launches each
 // share separately (see there).
-constexpr uint64_t kSplitShareBytes = 300'000'000;
+#ifndef QRS_SPLIT_SHARE_BYTES
+#define QRS_SPLIT_SHARE_BYTES 300000000ull
+#endif
+constexpr uint64_t kSplitShareBytes = QRS_SPLIT_SHARE_BYTES;
 
 // H is 128-aligned and in [1024, 8192].
 bool valid_h(int64_t h) { return h >= 1024 && h <= 8192 && h % 128 == 0; }
