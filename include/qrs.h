@@ -35,6 +35,12 @@
  *
  * Errors: every call returns a qrs_status. On failure, qrs_last_error()
  * returns a human-readable message for the calling thread.
+ *
+ * Throughput note: one launch has a fixed cost of a few microseconds (ramp
+ * up and drain). A caller with independent shares (different batches or
+ * buckets) can alternate them over two streams of the same priority to
+ * overlap that cost; on MI355X that raised the W=8, H=8192 MX share from
+ * about 6.1 to 6.5 TB/s. More streams did not help further.
  */
 #ifndef QRS_H_
 #define QRS_H_
