@@ -57,7 +57,11 @@ typedef enum qrs_status {
   QRS_ERR_INVALID_ARG = 1, /* a parameter breaks a documented constraint   */
   QRS_ERR_UNSUPPORTED = 2, /* a format the library does not implement      */
   QRS_ERR_HIP = 3,         /* the HIP runtime reported an error at launch  */
-  QRS_ERR_OUT_OF_MEMORY = 4 /* a host allocation for a plan failed        */
+  QRS_ERR_OUT_OF_MEMORY = 4, /* a host allocation for a plan failed       */
+  /* Range markers, not statuses: they make every int a value of the type,
+   * so a caller may pass any int and the library rejects it as a value. */
+  QRS_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  QRS_STATUS_RANGE_MAX_ = 2147483647
 } qrs_status;
 
 /* Element format of x (page "aclnnQuantReduceScatter", Constraints).
@@ -68,7 +72,9 @@ typedef enum qrs_x_dtype {
   QRS_X_INT8 = 0,       /* two's complement byte                         */
   QRS_X_FP8_E4M3FN = 1, /* OCP E4M3 "FN": bias 7, no inf, max 448        */
   QRS_X_FP8_E5M2 = 2,   /* OCP E5M2: bias 15, inf/NaN, max 57344         */
-  QRS_X_HIFLOAT8 = 3    /* reserved                                      */
+  QRS_X_HIFLOAT8 = 3,   /* reserved                                      */
+  QRS_X_DTYPE_RANGE_MIN_ = -2147483647 - 1, /* range markers, not formats  */
+  QRS_X_DTYPE_RANGE_MAX_ = 2147483647
 } qrs_x_dtype;
 
 /* Scale layout (same page, Constraints). Groups and blocks run along H
@@ -81,7 +87,9 @@ typedef enum qrs_x_dtype {
  * elements of x). */
 typedef enum qrs_scale_layout {
   QRS_SCALE_F32_GROUP128 = 0,
-  QRS_SCALE_E8M0_BLOCK32 = 1
+  QRS_SCALE_E8M0_BLOCK32 = 1,
+  QRS_SCALE_LAYOUT_RANGE_MIN_ = -2147483647 - 1, /* range markers, not layouts */
+  QRS_SCALE_LAYOUT_RANGE_MAX_ = 2147483647
 } qrs_scale_layout;
 
 /* Output type. The page's output dtype table did not survive extraction;
@@ -92,7 +100,9 @@ typedef enum qrs_scale_layout {
 typedef enum qrs_out_dtype {
   QRS_OUT_F32 = 0,  /* float32 [rows, H]                                 */
   QRS_OUT_BF16 = 1, /* bfloat16 [rows, H], round-to-nearest-even of fp32 */
-  QRS_OUT_F16 = 2   /* IEEE binary16 [rows, H], round-to-nearest-even    */
+  QRS_OUT_F16 = 2,  /* IEEE binary16 [rows, H], round-to-nearest-even    */
+  QRS_OUT_DTYPE_RANGE_MIN_ = -2147483647 - 1, /* range markers, not types  */
+  QRS_OUT_DTYPE_RANGE_MAX_ = 2147483647
 } qrs_out_dtype;
 
 typedef struct qrs_plan_s* qrs_plan_t;

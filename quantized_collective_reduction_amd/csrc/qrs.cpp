@@ -85,6 +85,7 @@ const char* qrs_status_string(qrs_status status) {
     case QRS_ERR_UNSUPPORTED: return "QRS_ERR_UNSUPPORTED";
     case QRS_ERR_HIP: return "QRS_ERR_HIP";
     case QRS_ERR_OUT_OF_MEMORY: return "QRS_ERR_OUT_OF_MEMORY";
+    default: break;
   }
   return "QRS_ERR_UNKNOWN";
 }
@@ -279,6 +280,14 @@ qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t
   const int64_t g = f32_scales ? 128 : 32;
   const int64_t sb = f32_scales ? 4 : 1;
   const int64_t ob = plan->out_format == qrs::kOutF32 ? 4 : 2;
+  // Lower bounds first, so that every product below is of positive values.
+  if (x_row_stride < h || x_row_stride % 16)
+    return fail(QRS_ERR_INVALID_ARG, "x_row_stride %lld: must be >= h and a multiple of 16 bytes",
+                static_cast<long long>(x_row_stride));
+  if (scale_row_stride < h / g)
+    return fail(QRS_ERR_INVALID_ARG, "scale_row_stride %lld: must be >= h / %lld", static_cast<long long>(scale_row_stride),
+                static_cast<long long>(g));
+  if (out_row_stride < h) return fail(QRS_ERR_INVALID_ARG, "out_row_stride %lld: must be >= h", static_cast<long long>(out_row_stride));
   // Every address the kernel forms must stay well inside 64 bits: bound the
   // byte extent of each tensor (rows - 1 strides plus one row) by 2^48.
   // Compare before multiplying so the check itself cannot overflow.
@@ -290,14 +299,8 @@ qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t
   if (rows >= stride_limit) return fail(QRS_ERR_INVALID_ARG, "%lld rows: must be below 2^32", static_cast<long long>(rows));
   if (x_row_stride >= stride_limit || scale_row_stride * sb >= stride_limit || out_row_stride * ob >= stride_limit)
     return fail(QRS_ERR_INVALID_ARG, "row strides must be below 4 GiB");
-  if (x_row_stride < h || x_row_stride % 16)
-    return fail(QRS_ERR_INVALID_ARG, "x_row_stride %lld: must be >= h and a multiple of 16 bytes",
-                static_cast<long long>(x_row_stride));
-  if (scale_row_stride < h / g)
-    return fail(QRS_ERR_INVALID_ARG, "scale_row_stride %lld: must be >= h / %lld", static_cast<long long>(scale_row_stride),
-                static_cast<long long>(g));
-  if (out_row_stride < h || (out_row_stride * ob) % 16)
-    return fail(QRS_ERR_INVALID_ARG, "out_row_stride %lld: must be >= h and span a multiple of 16 bytes",
+  if ((out_row_stride * ob) % 16)
+    return fail(QRS_ERR_INVALID_ARG, "out_row_stride %lld: must span a multiple of 16 bytes",
                 static_cast<long long>(out_row_stride));
   if (!aligned(out, 16)) return fail(QRS_ERR_INVALID_ARG, "out is not 16-byte aligned");
   // Extents actually addressed (last row ends at its h-th element).
