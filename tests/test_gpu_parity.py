@@ -83,12 +83,16 @@ def test_sweep_small_ragged(gpu, x_format, scale_layout, out_dtype, w, h):
 
 
 @pytest.mark.parametrize("rows", [1, 2, 7, 63, 64, 65, 257])
-def test_row_counts_around_block_edges(gpu, rows):
-    wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=8 * rows, h=1152)
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("base", ["w8_bs16384_h8192_mx_e4m3_bf16", "w8_bs8192_h7168_e5m2_bf16"])
+def test_row_counts_around_block_edges(gpu, rows, out_dtype, base):
+    # H = 1152 is 72 chunks a row: waves and blocks end mid-row and the grid's
+    # last wave is partial, for every store path (direct, LDS-staged, swapped).
+    wl = workloads.WORKLOADS[base].with_(bs=8 * rows, h=1152, out_dtype=out_dtype)
     xs, ss = workloads.generate(wl)
-    got = run_gpu(8, rows, 1152, wl.x_format, wl.scale_layout, "f32", xs, ss)
-    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, "f32"), "f32")
-    assert_parity(got, want, "f32", f"rows={rows}")
+    got = run_gpu(8, rows, 1152, wl.x_format, wl.scale_layout, out_dtype, xs, ss)
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, out_dtype), out_dtype)
+    assert_parity(got, want, out_dtype, f"rows={rows}")
 
 
 def test_non_finite_and_extreme_codes(gpu):
