@@ -113,7 +113,8 @@ typedef struct qrs_plan_s* qrs_plan_t;
  *   world_size  W, the communicator size: 2, 4 or 8 (Constraints).
  *   bs          tokens per rank before the all-to-all (x is [BS, H] on each
  *               rank, Constraints); must be > 0 (no empty input) and a
- *               multiple of W. This GPU's share has rows = bs / W.
+ *               multiple of W. This GPU's share has rows = bs / W, and
+ *               rows * h may not exceed 2^40 elements.
  *   h           hidden size: a multiple of 128 in [1024, 8192] (Constraints).
  *   x_dtype, scale_layout, out_dtype
  *               a pair that selects a mode of the page: MX needs an FP8 x;
