@@ -144,7 +144,10 @@ def _check(status):
 
 def _enum(value, names, enum_cls):
     if isinstance(value, str):
-        return names[value.lower()]
+        key = value.lower()
+        if key not in names:
+            raise ValueError(f"unknown {enum_cls.__name__} {value!r}; expected one of {sorted(names)}")
+        return names[key]
     return enum_cls(value) if value in enum_cls._value2member_map_ else int(value)
 
 
@@ -219,6 +222,38 @@ def alloc_slices(p: Plan, device="cuda", full_inputs=False):
     return xs, ss
 
 
+def _element_dtypes():
+    """torch element types of the codes, scales and outputs each mode names."""
+    import torch
+
+    return (
+        {XDtype.INT8: torch.int8, XDtype.FP8_E4M3FN: torch.float8_e4m3fn, XDtype.FP8_E5M2: torch.float8_e5m2},
+        {ScaleLayout.F32_GROUP128: torch.float32, ScaleLayout.E8M0_BLOCK32: torch.float8_e8m0fnu},
+        {OutDtype.F32: torch.float32, OutDtype.BF16: torch.bfloat16, OutDtype.F16: torch.float16},
+    )
+
+
+def _check_dtype(t, want, what):
+    """A tensor with a floating-point element type must have the one the mode
+    names (a float16 tensor handed a bf16 result would hold wrong values);
+    integer tensors are taken as raw bytes. Raw pointers are not checked, nor
+    modes the library rejects anyway (want is None)."""
+    if isinstance(t, int) or want is None or t.dtype == want:
+        return
+    if t.dtype.is_floating_point or t.dtype.is_complex:
+        raise ValueError(f"{what}: dtype {t.dtype} does not match the mode's {want}")
+
+
+def _check_plan_dtypes(p, xs, ss, outs, x_what, s_what, o_what):
+    x_dt, s_dt, o_dt = _element_dtypes()
+    for r, t in enumerate(xs):
+        _check_dtype(t, x_dt.get(p.x_dtype), f"{x_what} {r}")
+    for r, t in enumerate(ss):
+        _check_dtype(t, s_dt.get(p.scale_layout), f"{s_what} {r}")
+    for r, t in enumerate(outs):
+        _check_dtype(t, o_dt.get(p.out_dtype), o_what if len(outs) == 1 else f"{o_what} {r}")
+
+
 def _ptr(t):
     if isinstance(t, int):
         return t
@@ -258,6 +293,7 @@ def run(p: Plan, x_slices, scale_slices, out, stream=None):
         _check_tensor(x_slices[r], n, f"x slice {r}")
         _check_tensor(scale_slices[r], scale_bytes, f"scale slice {r}")
     _check_tensor(out, n * (4 if p.out_dtype == OutDtype.F32 else 2), "out")
+    _check_plan_dtypes(p, x_slices, scale_slices, [out], "x slice", "scale slice", "out")
     xs = (ctypes.c_void_p * w)(*[_ptr(t) for t in x_slices])
     ss = (ctypes.c_void_p * w)(*[_ptr(t) for t in scale_slices])
     _check(lib.qrs_run(p.handle, xs, ss, _ptr(out), None, 0, _stream_handle(stream)))
@@ -291,6 +327,7 @@ def run_strided(p: Plan, x_slices, scale_slices, out, stream=None):
     ld_x = _row_stride(x_slices, p.rows, p.h, "x slices")
     ld_s = _row_stride(scale_slices, p.rows, p.h // p.group, "scale slices")
     ld_o = _row_stride([out], p.rows, p.h, "out")
+    _check_plan_dtypes(p, x_slices, scale_slices, [out], "x slice", "scale slice", "out")
     xs = (ctypes.c_void_p * w)(*[t.data_ptr() for t in x_slices])
     ss = (ctypes.c_void_p * w)(*[t.data_ptr() for t in scale_slices])
     _check(lib.qrs_run_strided(p.handle, xs, ld_x * x_slices[0].element_size(), ss, ld_s, out.data_ptr(), ld_o,
@@ -313,10 +350,20 @@ def run_all_shares(p: Plan, x_full, scale_full, out_shares, stream=None):
         _check_tensor(x_full[r], n * w, f"x of rank {r}")
         _check_tensor(scale_full[r], scale_bytes * w, f"scales of rank {r}")
         _check_tensor(out_shares[r], n * (4 if p.out_dtype == OutDtype.F32 else 2), f"output of share {r}")
+    _check_plan_dtypes(p, x_full, scale_full, out_shares, "x of rank", "scales of rank", "output of share")
     xs = (ctypes.c_void_p * w)(*[_ptr(t) for t in x_full])
     ss = (ctypes.c_void_p * w)(*[_ptr(t) for t in scale_full])
     os_ = (ctypes.c_void_p * w)(*[_ptr(t) for t in out_shares])
     _check(lib.qrs_run_all_shares(p.handle, xs, ss, os_, None, 0, _stream_handle(stream)))
+
+
+def _check_quantize_dtypes(x_bf16, x_codes, scales, xd, sl):
+    import torch
+
+    x_dt, s_dt, _ = _element_dtypes()
+    _check_dtype(x_bf16, torch.bfloat16, "x_bf16")
+    _check_dtype(x_codes, x_dt.get(xd), "x_codes")
+    _check_dtype(scales, s_dt.get(sl), "scales")
 
 
 def quantize(x_bf16, x_codes, scales, x_dtype, scale_layout, stream=None):
@@ -333,6 +380,7 @@ def quantize(x_bf16, x_codes, scales, x_dtype, scale_layout, stream=None):
     _check_tensor(x_bf16, 2 * n, "x_bf16")
     _check_tensor(x_codes, n, "x_codes")
     _check_tensor(scales, n // 128 * 4 if sl == ScaleLayout.F32_GROUP128 else n // 32, "scales")
+    _check_quantize_dtypes(x_bf16, x_codes, scales, xd, sl)
     _check(lib.qrs_quantize(tokens, h, int(xd), int(sl), _ptr(x_bf16), _ptr(x_codes), _ptr(scales),
                             _stream_handle(stream)))
 
@@ -353,6 +401,7 @@ class Launch:
             _check_tensor(x_slices[r], n, f"x slice {r}")
             _check_tensor(scale_slices[r], scale_bytes, f"scale slice {r}")
         _check_tensor(out, n * (4 if p.out_dtype == OutDtype.F32 else 2), "out")
+        _check_plan_dtypes(p, x_slices, scale_slices, [out], "x slice", "scale slice", "out")
         self._plan = p  # keeps the plan alive
         self._keep = (list(x_slices), list(scale_slices), out)  # keeps the buffers alive
         self._xs = (ctypes.c_void_p * w)(*[_ptr(t) for t in x_slices])
@@ -379,6 +428,7 @@ class StridedLaunch:
         self._ld_x = _row_stride(x_slices, p.rows, p.h, "x slices") * x_slices[0].element_size()
         self._ld_s = _row_stride(scale_slices, p.rows, p.h // p.group, "scale slices")
         self._ld_o = _row_stride([out], p.rows, p.h, "out")
+        _check_plan_dtypes(p, x_slices, scale_slices, [out], "x slice", "scale slice", "out")
         self._plan = p
         self._keep = (list(x_slices), list(scale_slices), out)
         self._xs = (ctypes.c_void_p * w)(*[t.data_ptr() for t in x_slices])
@@ -409,6 +459,7 @@ class AllSharesLaunch:
             _check_tensor(x_full[r], n * w, f"x of rank {r}")
             _check_tensor(scale_full[r], scale_bytes * w, f"scales of rank {r}")
             _check_tensor(out_shares[r], n * (4 if p.out_dtype == OutDtype.F32 else 2), f"output of share {r}")
+        _check_plan_dtypes(p, x_full, scale_full, out_shares, "x of rank", "scales of rank", "output of share")
         self._plan = p
         self._keep = (list(x_full), list(scale_full), list(out_shares))
         self._xs = (ctypes.c_void_p * w)(*[_ptr(t) for t in x_full])
@@ -436,6 +487,7 @@ class QuantizeLaunch:
         _check_tensor(x_bf16, 2 * n, "x_bf16")
         _check_tensor(x_codes, n, "x_codes")
         _check_tensor(scales, n // 128 * 4 if self._sl == ScaleLayout.F32_GROUP128 else n // 32, "scales")
+        _check_quantize_dtypes(x_bf16, x_codes, scales, self._xd, self._sl)
         self._keep = (x_bf16, x_codes, scales)
         self._args = (tokens, h, self._xd, self._sl, _ptr(x_bf16), _ptr(x_codes), _ptr(scales),
                       ctypes.c_void_p(_stream_handle(stream)))

@@ -184,6 +184,49 @@ def test_prepared_launch_checks_arguments_on_host(lib):
         qrs.Launch(p, x, s, torch.zeros(16, 1024, dtype=torch.float32))  # wrong output size
 
 
+def test_binding_rejects_floating_dtypes_other_than_the_modes():
+    """Typed tensors must carry the element types the mode names (integer
+    tensors are raw bytes). The dtype check runs before any pointer is taken,
+    so host tensors reach it."""
+    import torch
+
+    p = qrs.plan(2, 32, 1024, "e4m3fn", "e8m0_block32", "bf16")
+    x = [torch.zeros(16, 1024, dtype=torch.uint8) for _ in range(2)]
+    s = [torch.zeros(16, 32, dtype=torch.uint8) for _ in range(2)]
+    for bad_out in (torch.zeros(16, 1024, dtype=torch.float16), torch.zeros(16, 512, dtype=torch.float32)):
+        with pytest.raises(ValueError, match="does not match"):
+            qrs.run(p, x, s, bad_out)
+        with pytest.raises(ValueError, match="does not match"):
+            qrs.Launch(p, x, s, bad_out)
+    out = torch.zeros(16, 1024, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="x slice 1"):
+        qrs.run(p, [x[0], torch.zeros(16, 1024, dtype=torch.float8_e5m2)], s, out)
+    with pytest.raises(ValueError, match="scale slice 0"):
+        qrs.run(p, x, [torch.zeros(16, 32, dtype=torch.float8_e4m3fn), s[1]], out)
+    # Matching float8 and E8M0 dtypes pass the dtype check and fail only at the host-tensor check.
+    with pytest.raises(ValueError, match="device tensors only"):
+        qrs.run(p, [t.view(torch.float8_e4m3fn) for t in x], [t.view(torch.float8_e8m0fnu) for t in s], out)
+
+    pg = qrs.plan(2, 32, 1024, "e5m2", "f32_group128", "f32")
+    xg = [torch.zeros(32, 1024, dtype=torch.uint8) for _ in range(2)]
+    sg = [torch.zeros(32, 8, dtype=torch.float32) for _ in range(2)]
+    outs = [torch.zeros(16, 512, dtype=torch.bfloat16), torch.zeros(16, 1024, dtype=torch.float32)]
+    with pytest.raises(ValueError, match="output of share 0"):
+        qrs.run_all_shares(pg, xg, sg, outs)
+    with pytest.raises(ValueError, match="scales of rank 1"):
+        qrs.AllSharesLaunch(pg, xg, [sg[0], torch.zeros(32, 4, dtype=torch.float64)], [outs[1], outs[1]])
+
+    xb = torch.zeros(16, 1024, dtype=torch.float16)
+    with pytest.raises(ValueError, match="x_bf16"):
+        qrs.quantize(xb, torch.zeros(16, 1024, dtype=torch.uint8), torch.zeros(16, 32, dtype=torch.uint8),
+                     "e4m3fn", "e8m0_block32")
+    with pytest.raises(ValueError, match="x_codes"):
+        qrs.QuantizeLaunch(xb.view(torch.bfloat16), torch.zeros(16, 1024, dtype=torch.float8_e5m2),
+                           torch.zeros(16, 32, dtype=torch.uint8), "e4m3fn", "e8m0_block32")
+    with pytest.raises(ValueError, match="unknown XDtype"):
+        qrs.plan(2, 32, 1024, "fp8", "f32_group128", "f32")
+
+
 def test_strided_run_rejects_bad_strides_on_host(fake_ptr_lib):
     lib = fake_ptr_lib
     p = qrs.plan(2, 32, 1024, "e4m3fn", "e8m0_block32", "f32")
