@@ -1,7 +1,8 @@
 """Benchmark: achieved HBM bandwidth of one GPU's share of the quantized
 reduce-scatter (dequant + rank-ordered reduce) on MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--op OP] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--op OP] [--layout L]
+                    [--hot] [--no-cpu-baseline] [--gpus 1]
 
 A step is one launch of the whole hot path (decode, scale, rank-ordered fp32
 fold, convert, store) over one batch: W rank slices of the workload, already
@@ -24,7 +25,16 @@ Prints ONE JSON line on stdout:
                    rocprofv3 counter summaries, when they match this kernel
                    source (else null);
   cpu_baseline     the CPU oracle timed on the host (single thread) on the
-                   same workload.
+                   same workload;
+  cpu_baseline_all_cores
+                   the same oracle calls on row blocks of the share, spread
+                   over the host's cores (at most 16 threads; the result does
+                   not depend on the blocking);
+  copy_calibration the plain 16-byte stream copy of the same bytes, timed the
+                   same way as the steps (rotating buffers, back to back);
+  hot              with --hot, context only: K more launches on one
+                   input/output set (no rotation, so a working set under
+                   256 MB may be served from the Infinity Cache); else null.
 Diagnostics go to stderr.
 """
 
@@ -111,6 +121,50 @@ def cpu_baseline(wl, xs, ss, min_seconds=10.0, min_reps=3):
         "kind": "oracle",
         "sample": f"whole {wl.name} share ({wl.rows}x{wl.h} outputs from {wl.world_size} rank slices), "
                   f"median of {len(times)} runs, {med:.3f} s each, numpy single thread",
+    }
+
+
+def _host_threads():
+    """Host cores this process may use, at most 16 (a GPU machine's CPU share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_baseline_all_cores(wl, xs, ss, min_seconds=5.0, min_reps=3, block_rows=64):
+    """Time the oracle over row blocks of the share on a thread pool: the
+    oracle computes every output element from its own row only, so the blocks
+    are independent (numpy releases the GIL inside its array operations)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    workers = _host_threads()
+    starts = range(0, wl.rows, block_rows)
+
+    def block(s):
+        return oracle.reduce_scatter_share([x[s:s + block_rows] for x in xs], [c[s:s + block_rows] for c in ss],
+                                           wl.x_format, wl.scale_layout, wl.out_dtype)
+
+    times = []
+    with ThreadPoolExecutor(workers) as ex:
+        t_start = time.perf_counter()
+        while len(times) < min_reps or time.perf_counter() - t_start < min_seconds:
+            t0 = time.perf_counter()
+            list(ex.map(block, starts))
+            times.append(time.perf_counter() - t0)
+            if len(times) >= 50:
+                break
+    med = statistics.median(times)
+    return {
+        "value": round(wl.algorithmic_bytes() / med / 1e9, 4),
+        "unit": "GB/s",
+        "cores": workers,
+        "kind": "oracle",
+        "sample": f"whole {wl.name} share in {block_rows}-row blocks on {workers} threads, "
+                  f"median of {len(times)} runs, {med:.3f} s each",
     }
 
 
@@ -241,7 +295,10 @@ def main():
     ap.add_argument("--layout", default="pitched", choices=["pitched", "packed", "separate"],
                     help="placement of the W rank slices: pitched (one buffer, the pitch qrs_slice_pitch "
                          "recommends; default), packed (one buffer, back to back), separate (one allocation each)")
-    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (cpu_baseline = null)")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle timings (cpu_baseline and cpu_baseline_all_cores = null)")
+    ap.add_argument("--hot", action="store_true",
+                    help="also time K launches on one input/output set, without rotation (context only)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -299,26 +356,42 @@ def main():
     log(f"[bench] {args.steps} steps in {wall * 1e3:.2f} ms wall; HIP events over the region: "
         f"{avg_launch_s * 1e6:.2f} us per launch")
 
-    # Calibration: the plain 16-byte stream copy of the same read+write volume.
+    hot_s = None
+    if args.hot:
+        # Context: the same launches on one set, no rotation. Opt-in, so that
+        # a kernel trace of the default command averages rotated launches only.
+        hot = launches[0]
+        for _ in range(min(args.warmup, 20)):
+            hot()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            hot()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        hot_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
+        log(f"[bench] hot (one set, no rotation): {hot_s * 1e6:.2f} us per launch")
+
+    # Calibration: the plain 16-byte stream copy of the same read+write
+    # volume, rotating over n_sets buffer pairs and timed like the steps.
     copy_bytes = (alg_bytes // 2) // 16 * 16
     src = torch.empty(copy_bytes * n_sets, dtype=torch.uint8, device=dev)
     dst = torch.empty_like(src)
-    c_starts = [torch.cuda.Event(enable_timing=True) for _ in range(50)]
-    c_ends = [torch.cuda.Event(enable_timing=True) for _ in range(50)]
-    for i in range(60):
-        k = i % n_sets
-        j = i - 10
-        if j >= 0:
-            c_starts[j].record(stream)
-        qrs.stream_copy(src[k * copy_bytes:(k + 1) * copy_bytes], dst[k * copy_bytes:(k + 1) * copy_bytes],
-                        stream=stream)
-        if j >= 0:
-            c_ends[j].record(stream)
+    copies = [(src[k * copy_bytes:(k + 1) * copy_bytes], dst[k * copy_bytes:(k + 1) * copy_bytes])
+              for k in range(n_sets)]
+    n_copies = max(50, min(args.steps, 1000))
+    for i in range(10):
+        qrs.stream_copy(*copies[i % n_sets], stream=stream)
     torch.cuda.synchronize()
-    copy_s = statistics.fmean(s.elapsed_time(e) for s, e in zip(c_starts, c_ends)) / 1e3
+    ev0.record(stream)
+    for i in range(n_copies):
+        qrs.stream_copy(*copies[i % n_sets], stream=stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    copy_s = ev0.elapsed_time(ev1) / 1e3 / n_copies
     copy_gbps = 2 * copy_bytes / copy_s / 1e9
     log(f"[bench] stream-copy calibration: {2 * copy_bytes} bytes moved in {copy_s * 1e6:.2f} us = {copy_gbps:.0f} GB/s")
-    del src, dst
+    del src, dst, copies
 
     achieved = alg_bytes / avg_launch_s / 1e9
     value = alg_bytes * args.steps / wall / 1e9
@@ -362,13 +435,20 @@ def main():
             "traffic": read_traffic(wl.name, args.op),
             "kernel_us_avg": round(avg_launch_s * 1e6, 3),
         },
-        "copy_calibration": {"bytes_moved": 2 * copy_bytes, "GBps": round(copy_gbps, 1)},
+        "copy_calibration": {"bytes_moved": 2 * copy_bytes, "us": round(copy_s * 1e6, 3),
+                             "GBps": round(copy_gbps, 1)},
+        "hot": None if hot_s is None else {
+            "kernel_us_avg": round(hot_s * 1e6, 3), "GBps": round(alg_bytes / hot_s / 1e9, 2),
+            "note": "context only: one input/output set, no rotation"},
         "cpu_baseline": None,
+        "cpu_baseline_all_cores": None,
     }
     if not args.no_cpu_baseline and host_inputs is not None:
         log("[bench] timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(wl, *host_inputs)
         log(f"[bench] cpu baseline: {result['cpu_baseline']}")
+        result["cpu_baseline_all_cores"] = cpu_baseline_all_cores(wl, *host_inputs)
+        log(f"[bench] cpu baseline, all cores: {result['cpu_baseline_all_cores']}")
     print(json.dumps(result), flush=True)
 
 

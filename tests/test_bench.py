@@ -48,6 +48,31 @@ def test_cpu_baseline_fields():
     assert cb["value"] > 0 and cb["unit"] == "GB/s" and cb["cores"] == 1 and cb["kind"] == "oracle"
 
 
+def test_cpu_baseline_all_cores_fields():
+    wl = workloads.WORKLOADS["w2_bs32_h1024_int8_f32"]
+    xs, ss = workloads.generate(wl)
+    cb = bench.cpu_baseline_all_cores(wl, xs, ss, min_seconds=0.0, min_reps=3, block_rows=4)
+    assert set(cb) == {"value", "unit", "cores", "kind", "sample"}
+    assert cb["value"] > 0 and cb["unit"] == "GB/s" and 1 <= cb["cores"] <= 16 and cb["kind"] == "oracle"
+
+
+@pytest.mark.parametrize("name", ["w2_bs32_h1024_int8_f32", "w8_bs16384_h8192_mx_e4m3_bf16"])
+def test_oracle_row_blocks_concatenate_to_the_whole_share(name):
+    """The all-cores baseline runs the oracle on row blocks: that is the same
+    work only if the blocks' results, stacked, are the whole share's."""
+    import numpy as np
+
+    import oracle
+
+    wl = workloads.WORKLOADS[name]
+    wl = wl.with_(bs=wl.world_size * min(wl.rows, 12))
+    xs, ss = workloads.generate(wl)
+    whole = oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype)
+    parts = [oracle.reduce_scatter_share([x[s:s + 5] for x in xs], [c[s:s + 5] for c in ss], wl.x_format,
+                                         wl.scale_layout, wl.out_dtype) for s in range(0, wl.rows, 5)]
+    assert np.array_equal(np.concatenate(parts).view(np.uint8), whole.view(np.uint8))
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("op", ["share", "strided", "all_shares", "quantize"])
 def test_json_line(gpu, op):
@@ -64,6 +89,9 @@ def test_json_line(gpu, op):
     assert d["n_gpus"] == 1 and d["steps"] == 20 and d["warmup"] == 10
     assert d["value"] > 0 and d["unit"] == "GB/s" and d["higher_is_better"] is True
     assert d["vs_baseline"] is None and d["data"] == "synthetic" and d["cpu_baseline"] is None
+    assert d["cpu_baseline_all_cores"] is None and d["hot"] is None
+    c = d["copy_calibration"]
+    assert c["GBps"] > 0 and abs(c["GBps"] - c["bytes_moved"] / c["us"] / 1e3) < 0.01 * c["GBps"]
     assert d["config"]["workload"].startswith(wl) and d["config"]["op"] == op
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
