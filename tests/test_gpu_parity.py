@@ -235,6 +235,33 @@ def test_prepared_launch_matches_run(gpu):
     assert_parity(out_bits(o2), want, wl.out_dtype, "Launch")
 
 
+@pytest.mark.parametrize("x_format,scale_layout", [("e4m3fn", "e8m0_block32"), ("e5m2", "f32_group128"),
+                                                   ("int8", "f32_group128")])
+def test_typed_float8_tensors(gpu, x_format, scale_layout):
+    """The binding accepts codes and scales in torch's float8 / int8 / E8M0
+    dtypes as well as raw bytes; both give the oracle's bits."""
+    import quantized_collective_reduction_amd as qrs
+
+    x_dt = {"int8": torch.int8, "e4m3fn": torch.float8_e4m3fn, "e5m2": torch.float8_e5m2}[x_format]
+    base = {"int8": "w2_bs32_h1024_int8_f32", "e5m2": "w8_bs8192_h7168_e5m2_bf16",
+            "e4m3fn": "w8_bs16384_h8192_mx_e4m3_bf16"}[x_format]
+    wl = workloads.WORKLOADS[base].with_(world_size=4, bs=4 * 9, h=1024, out_dtype="bf16")
+    assert (wl.x_format, wl.scale_layout) == (x_format, scale_layout)
+    xs, ss = workloads.generate(wl)
+    p = qrs.plan(4, wl.bs, wl.h, x_format, scale_layout, "bf16")
+    dx, ds = to_device(xs, ss)
+    typed_x = [t.view(x_dt) for t in dx]
+    typed_s = [t.view(torch.float8_e8m0fnu) for t in ds] if scale_layout == "e8m0_block32" else ds
+    o_raw = empty_out(wl.rows, wl.h, "bf16")
+    o_typed = empty_out(wl.rows, wl.h, "bf16")
+    qrs.run(p, dx, ds, o_raw)
+    qrs.run(p, typed_x, typed_s, o_typed)
+    torch.cuda.synchronize()
+    assert np.array_equal(out_bits(o_raw), out_bits(o_typed))
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, x_format, scale_layout, "bf16"), "bf16")
+    assert_parity(out_bits(o_typed), want, "bf16", f"typed {x_format}/{scale_layout}")
+
+
 @pytest.mark.parametrize("full", [False, True])
 def test_recommended_slice_placement(gpu, full):
     """Slices placed by qrs.alloc_slices (one buffer, recommended pitch) give
