@@ -30,6 +30,9 @@ Prints ONE JSON line on stdout:
                    the same oracle calls on row blocks of the share, spread
                    over the host's cores (at most 16 threads; the result does
                    not depend on the blocking);
+  device_memory    the HBM bus width and memory clock the HIP runtime
+                   reports, and the peak they imply, beside the published
+                   8 TB/s that roofline.peak uses;
   copy_calibration the plain 16-byte stream copy of the same bytes, timed the
                    same way as the steps (rotating buffers, back to back);
   hot              with --hot, context only: K more launches on one
@@ -120,7 +123,7 @@ def cpu_baseline(wl, xs, ss, min_seconds=10.0, min_reps=3):
         "cores": 1,
         "kind": "oracle",
         "sample": f"whole {wl.name} share ({wl.rows}x{wl.h} outputs from {wl.world_size} rank slices), "
-                  f"median of {len(times)} runs, {med:.3f} s each, numpy single thread",
+                  f"median of {len(times)} runs, {med:.3f} s each, numpy single thread on {host_cpu_model()}",
     }
 
 
@@ -164,8 +167,49 @@ def cpu_baseline_all_cores(wl, xs, ss, min_seconds=5.0, min_reps=3, block_rows=6
         "cores": workers,
         "kind": "oracle",
         "sample": f"whole {wl.name} share in {block_rows}-row blocks on {workers} threads, "
-                  f"median of {len(times)} runs, {med:.3f} s each",
+                  f"median of {len(times)} runs, {med:.3f} s each, on {host_cpu_model()}",
     }
+
+
+def device_memory_props():
+    """The HBM figures the HIP runtime reports for device 0 (memory clock in
+    kHz, bus width in bits) and the peak they imply, next to the published
+    8 TB/s used for the roofline. The runtime reports HBM3E's memory clock as
+    a quarter of the per-pin data rate (2 GHz on MI355X, whose pins run at
+    8 Gb/s), so the implied peak is bus bytes x clock x 4. Read with
+    hipDeviceGetAttribute from the HIP runtime torch has loaded."""
+    import ctypes
+
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                path = line.split()[-1]
+                break
+    if path is None:
+        return None
+    hip = ctypes.CDLL(path)
+    attr_bus_width, attr_mem_clock = 59, 60  # hipDeviceAttributeMemoryBusWidth, ...MemoryClockRate
+    vals = {}
+    for name, attr in (("memory_bus_width_bits", attr_bus_width), ("memory_clock_khz", attr_mem_clock)):
+        v = ctypes.c_int(0)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, 0) != 0:
+            return None
+        vals[name] = v.value
+    vals["hbm_gbps_implied"] = round(vals["memory_bus_width_bits"] / 8 * vals["memory_clock_khz"] * 1e3 * 4 / 1e9, 1)
+    vals["hbm_gbps_published"] = HBM_PEAK_GBPS
+    return vals
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def place_inputs(p, xs, ss, dev, qrs, torch, layout, full_inputs=False):
@@ -435,6 +479,7 @@ def main():
             "traffic": read_traffic(wl.name, args.op),
             "kernel_us_avg": round(avg_launch_s * 1e6, 3),
         },
+        "device_memory": device_memory_props(),
         "copy_calibration": {"bytes_moved": 2 * copy_bytes, "us": round(copy_s * 1e6, 3),
                              "GBps": round(copy_gbps, 1)},
         "hot": None if hot_s is None else {

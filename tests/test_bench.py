@@ -90,6 +90,8 @@ def test_json_line(gpu, op):
     assert d["value"] > 0 and d["unit"] == "GB/s" and d["higher_is_better"] is True
     assert d["vs_baseline"] is None and d["data"] == "synthetic" and d["cpu_baseline"] is None
     assert d["cpu_baseline_all_cores"] is None and d["hot"] is None
+    m = d["device_memory"]
+    assert m is not None and m["memory_bus_width_bits"] > 0 and m["memory_clock_khz"] > 0
     c = d["copy_calibration"]
     assert c["GBps"] > 0 and abs(c["GBps"] - c["bytes_moved"] / c["us"] / 1e3) < 0.01 * c["GBps"]
     assert d["config"]["workload"].startswith(wl) and d["config"]["op"] == op
