@@ -36,6 +36,7 @@ __all__ = [
     "alloc_slices",
     "quantize",
     "Launch",
+    "StridedLaunch",
     "AllSharesLaunch",
     "QuantizeLaunch",
     "stream_copy",
@@ -316,6 +317,24 @@ def _row_stride(tensors, rows, cols, what):
     return strides.pop()
 
 
+def _strided_strides(p: Plan, x_slices, scale_slices, out):
+    """Row strides of ``run_strided``'s views, in the units qrs_run_strided
+    takes (bytes for x, scale elements, output elements). Each view's element
+    must be the size of the mode's element, since the library counts its
+    strides and row lengths in those."""
+    ld_x = _row_stride(x_slices, p.rows, p.h, "x slices")
+    ld_s = _row_stride(scale_slices, p.rows, p.h // p.group, "scale slices")
+    ld_o = _row_stride([out], p.rows, p.h, "out")
+    sizes = ((x_slices, 1, "x slices"),
+             (scale_slices, 4 if p.scale_layout == ScaleLayout.F32_GROUP128 else 1, "scale slices"),
+             ([out], 4 if p.out_dtype == OutDtype.F32 else 2, "out"))
+    for tensors, size, what in sizes:
+        for t in tensors:
+            if t.element_size() != size:
+                raise ValueError(f"{what}: {size}-byte elements expected for this plan, got {t.dtype}")
+    return ld_x, ld_s, ld_o
+
+
 def run_strided(p: Plan, x_slices, scale_slices, out, stream=None):
     """``run`` for 2-D views whose rows are not adjacent (row ranges of wider
     buffers, padded rows): x slices ``[rows, H]`` uint8, scale slices
@@ -324,14 +343,11 @@ def run_strided(p: Plan, x_slices, scale_slices, out, stream=None):
     w = p.world_size
     if len(x_slices) != w or len(scale_slices) != w:
         raise ValueError(f"need {w} x slices and {w} scale slices")
-    ld_x = _row_stride(x_slices, p.rows, p.h, "x slices")
-    ld_s = _row_stride(scale_slices, p.rows, p.h // p.group, "scale slices")
-    ld_o = _row_stride([out], p.rows, p.h, "out")
+    ld_x, ld_s, ld_o = _strided_strides(p, x_slices, scale_slices, out)
     _check_plan_dtypes(p, x_slices, scale_slices, [out], "x slice", "scale slice", "out")
     xs = (ctypes.c_void_p * w)(*[t.data_ptr() for t in x_slices])
     ss = (ctypes.c_void_p * w)(*[t.data_ptr() for t in scale_slices])
-    _check(lib.qrs_run_strided(p.handle, xs, ld_x * x_slices[0].element_size(), ss, ld_s, out.data_ptr(), ld_o,
-                               None, 0, _stream_handle(stream)))
+    _check(lib.qrs_run_strided(p.handle, xs, ld_x, ss, ld_s, out.data_ptr(), ld_o, None, 0, _stream_handle(stream)))
 
 
 def run_all_shares(p: Plan, x_full, scale_full, out_shares, stream=None):
@@ -425,9 +441,7 @@ class StridedLaunch:
         w = p.world_size
         if len(x_slices) != w or len(scale_slices) != w:
             raise ValueError(f"need {w} x slices and {w} scale slices")
-        self._ld_x = _row_stride(x_slices, p.rows, p.h, "x slices") * x_slices[0].element_size()
-        self._ld_s = _row_stride(scale_slices, p.rows, p.h // p.group, "scale slices")
-        self._ld_o = _row_stride([out], p.rows, p.h, "out")
+        self._ld_x, self._ld_s, self._ld_o = _strided_strides(p, x_slices, scale_slices, out)
         _check_plan_dtypes(p, x_slices, scale_slices, [out], "x slice", "scale slice", "out")
         self._plan = p
         self._keep = (list(x_slices), list(scale_slices), out)

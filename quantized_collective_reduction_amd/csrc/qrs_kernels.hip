@@ -582,19 +582,17 @@ hipError_t launch_typed(const ReduceLaunch& l, hipStream_t stream) {
   a.x_share_stride = l.x_share_stride / 16;
   a.scale_share_stride = l.scale_share_stride;
   const dim3 grid(static_cast<uint32_t>(blocks), l.n_shares);
+  const dim3 block(QRS_BLOCK);
   if (l.n_shares > 1) {
     if (l.n_rows != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF, kAddrShares>), grid, dim3(QRS_BLOCK), 0, stream, a);
-  } else if (l.n_rows > 1) {
-    hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF, kAddrRows>), grid, dim3(QRS_BLOCK), 0, stream, a);
-  } else if (a.chunks_per_row * OutPieces<OF>::kCount * sizeof(u32x4) < (1ull << 32)) {
-    // The output is the largest of the share's tensors (at least 2 bytes per
-    // element against 1 + 1/32 for a slice and its scales).
-    hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF, kAddrFlat32>), grid, dim3(QRS_BLOCK), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((reduce_kernel<W, XF, SL, OF, kAddrFlat>), grid, dim3(QRS_BLOCK), 0, stream, a);
+    return launch_kernel(reduce_kernel<W, XF, SL, OF, kAddrShares>, grid, block, stream, a);
   }
-  return hipGetLastError();
+  if (l.n_rows > 1) return launch_kernel(reduce_kernel<W, XF, SL, OF, kAddrRows>, grid, block, stream, a);
+  // The output is the largest of the share's tensors (at least 2 bytes per
+  // element against 1 + 1/32 for a slice and its scales).
+  if (a.chunks_per_row * OutPieces<OF>::kCount * sizeof(u32x4) < (1ull << 32))
+    return launch_kernel(reduce_kernel<W, XF, SL, OF, kAddrFlat32>, grid, block, stream, a);
+  return launch_kernel(reduce_kernel<W, XF, SL, OF, kAddrFlat>, grid, block, stream, a);
 }
 
 template <int W, int XF, int SL>
@@ -645,9 +643,8 @@ hipError_t launch_stream_copy(const void* src, void* dst, uint64_t bytes, hipStr
   const uint64_t n = bytes / 16;
   const uint64_t blocks = (n + 255) / 256;
   if (blocks == 0 || blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(stream_copy_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), 0, stream,
-                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
-  return hipGetLastError();
+  return launch_kernel(stream_copy_kernel, dim3(static_cast<uint32_t>(blocks)), dim3(256), stream,
+                       static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n);
 }
 
 }  // namespace qrs

@@ -10,6 +10,24 @@ namespace qrs {
 
 constexpr int kMaxWorld = 8;
 
+template <typename T>
+struct same_type {
+  using type = T;
+};
+
+// Enqueue kernel<<<grid, block, 0, stream>>>(args...) and return the status
+// of this launch itself. A triple-chevron launch returns nothing, and
+// reading hipGetLastError after it would also report an earlier, unrelated
+// failure of the calling thread as this launch's. Each argument takes the
+// exact type of its kernel parameter, so the bytes handed to the runtime
+// are the parameter's.
+template <typename... Params>
+inline hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block, hipStream_t stream,
+                                typename same_type<Params>::type... args) {
+  void* arg_ptrs[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, arg_ptrs, 0, stream);
+}
+
 // Element and scale formats as the kernels see them.
 enum XFormat : int { kXInt8 = 0, kXE4M3FN = 1, kXE5M2 = 2 };
 enum ScaleLayout : int { kScaleF32Group128 = 0, kScaleE8M0Block32 = 1 };

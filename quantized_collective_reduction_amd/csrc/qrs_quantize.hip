@@ -206,9 +206,8 @@ hipError_t launch_typed(const void* in, void* codes, void* scales, uint64_t n_el
   const uint64_t per_block = static_cast<uint64_t>(kBlock) * QRS_Q_PIECES;
   const uint64_t blocks = (n_lanes + per_block - 1) / per_block;
   if (blocks == 0 || blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((quantize_kernel<XF, SL>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream,
-                     static_cast<const u32x4*>(in), static_cast<u32x2*>(codes), scales, n_lanes);
-  return hipGetLastError();
+  return launch_kernel(quantize_kernel<XF, SL>, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), stream,
+                       static_cast<const u32x4*>(in), static_cast<u32x2*>(codes), scales, n_lanes);
 }
 
 }  // namespace

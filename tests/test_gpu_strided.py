@@ -81,6 +81,28 @@ def test_strided_rejects_mismatched_strides(gpu):
         qrs.run_strided(p, [a[:, :1024], b[:, :1024]], s, out)
 
 
+def test_strided_rejects_element_sizes_of_another_mode(gpu):
+    # The strides and row lengths are counted in the mode's elements: a view
+    # of 1-byte elements as the bf16 output (or as fp32 scales) would make the
+    # kernel address twice (four times) the view's rows. Rejected before any
+    # launch, as are Launch objects built from them.
+    p = qrs.plan(2, 8, 1024, "e4m3fn", "f32_group128", "bf16")
+    xs = [torch.zeros(4, 1024, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    s32 = [torch.zeros(4, 8, dtype=torch.float32, device="cuda") for _ in range(2)]
+    s8 = [torch.zeros(4, 8, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    out16 = torch.zeros(4, 1024, dtype=torch.bfloat16, device="cuda")
+    out8 = torch.zeros(4, 1024, dtype=torch.uint8, device="cuda")
+    x16 = [torch.zeros(4, 1024, dtype=torch.int16, device="cuda") for _ in range(2)]
+    for bad in ((xs, s32, out8), (xs, s8, out16), (x16, s32, out16)):
+        with pytest.raises(ValueError, match="elements expected"):
+            qrs.run_strided(p, *bad)
+        with pytest.raises(ValueError, match="elements expected"):
+            qrs.StridedLaunch(p, *bad)
+    qrs.run_strided(p, xs, s32, out16)  # the matching sizes are accepted
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out16.view(torch.int16)) == 0
+
+
 @pytest.mark.parametrize("h,rows", [(1152, 61), (7168, 9), (5120, 13), (1024, 33)])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 def test_rows_crossing_waves_and_blocks(gpu, h, rows, out_dtype):
