@@ -37,7 +37,11 @@ Prints ONE JSON line on stdout:
                    same way as the steps (rotating buffers, back to back);
   hot              with --hot, context only: K more launches on one
                    input/output set (no rotation, so a working set under
-                   256 MB may be served from the Infinity Cache); else null.
+                   256 MB may be served from the Infinity Cache); else null;
+  overlap_2streams with --overlap, context only: K more steps alternated
+                   over two streams of the default priority (independent
+                   batches, each stream on its own rotating sets), wall
+                   time per step; else null.
 Diagnostics go to stderr.
 """
 
@@ -343,6 +347,8 @@ def main():
                     help="skip the oracle timings (cpu_baseline and cpu_baseline_all_cores = null)")
     ap.add_argument("--hot", action="store_true",
                     help="also time K launches on one input/output set, without rotation (context only)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="also time K independent steps alternated over two streams (context only)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -416,6 +422,32 @@ def main():
         hot_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
         log(f"[bench] hot (one set, no rotation): {hot_s * 1e6:.2f} us per launch")
 
+    overlap = None
+    if args.overlap:
+        # Context: independent steps alternated over two streams (both of
+        # the default priority), so that one launch's ramp-up overlaps the
+        # previous one's drain. Each stream keeps to its own input/output
+        # sets (an even number of them), so no two launches in flight share
+        # a buffer. Wall time over the K steps, like value.
+        s2 = torch.cuda.Stream(device=dev)
+        n_even = n_sets - n_sets % 2
+        pair = [launches[k] if k % 2 == 0 else launches[k].on_stream(s2) for k in range(n_even)]
+        for i in range(min(args.warmup, 20) + n_even):
+            pair[i % n_even]()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            pair[i % n_even]()
+        torch.cuda.synchronize()
+        wall2 = time.perf_counter() - t0
+        overlap = {"us_per_step": round(wall2 / args.steps * 1e6, 3),
+                   "GBps": round(alg_bytes * args.steps / wall2 / 1e9, 2),
+                   "sets_per_stream": n_even // 2,
+                   "note": "context only: independent steps alternated over two default-priority streams; "
+                           "value and roofline describe one launch at a time"}
+        log(f"[bench] two streams: {overlap['us_per_step']:.2f} us per step = {overlap['GBps']:.0f} GB/s")
+        del pair, s2
+
     # Calibration: the plain 16-byte stream copy of the same read+write
     # volume, rotating over n_sets buffer pairs and timed like the steps.
     copy_bytes = (alg_bytes // 2) // 16 * 16
@@ -482,6 +514,7 @@ def main():
         "device_memory": device_memory_props(),
         "copy_calibration": {"bytes_moved": 2 * copy_bytes, "us": round(copy_s * 1e6, 3),
                              "GBps": round(copy_gbps, 1)},
+        "overlap_2streams": overlap,
         "hot": None if hot_s is None else {
             "kernel_us_avg": round(hot_s * 1e6, 3), "GBps": round(alg_bytes / hot_s / 1e9, 2),
             "note": "context only: one input/output set, no rotation"},

@@ -427,6 +427,10 @@ class Launch:
         self._fn = lib.qrs_run
         self._handle = p.handle
 
+    def on_stream(self, stream):
+        """The same launch (plan and buffers) enqueued on another stream."""
+        return Launch(self._plan, *self._keep, stream=stream)
+
     def __call__(self):
         status = self._fn(self._handle, self._xs, self._ss, self._out, None, 0, self._stream)
         if status:
@@ -451,6 +455,10 @@ class StridedLaunch:
         self._stream = ctypes.c_void_p(_stream_handle(stream))
         self._fn = lib.qrs_run_strided
         self._handle = p.handle
+
+    def on_stream(self, stream):
+        """The same launch (plan and views) enqueued on another stream."""
+        return StridedLaunch(self._plan, *self._keep, stream=stream)
 
     def __call__(self):
         status = self._fn(self._handle, self._xs, self._ld_x, self._ss, self._ld_s, self._out, self._ld_o, None, 0,
@@ -483,6 +491,10 @@ class AllSharesLaunch:
         self._fn = lib.qrs_run_all_shares
         self._handle = p.handle
 
+    def on_stream(self, stream):
+        """The same launch (plan and buffers) enqueued on another stream."""
+        return AllSharesLaunch(self._plan, *self._keep, stream=stream)
+
     def __call__(self):
         status = self._fn(self._handle, self._xs, self._ss, self._os, None, 0, self._stream)
         if status:
@@ -506,6 +518,10 @@ class QuantizeLaunch:
         self._args = (tokens, h, self._xd, self._sl, _ptr(x_bf16), _ptr(x_codes), _ptr(scales),
                       ctypes.c_void_p(_stream_handle(stream)))
         self._fn = lib.qrs_quantize
+
+    def on_stream(self, stream):
+        """The same launch (mode and buffers) enqueued on another stream."""
+        return QuantizeLaunch(*self._keep, self._xd, self._sl, stream=stream)
 
     def __call__(self):
         status = self._fn(*self._args)

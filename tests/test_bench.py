@@ -89,7 +89,7 @@ def test_json_line(gpu, op):
     assert d["n_gpus"] == 1 and d["steps"] == 20 and d["warmup"] == 10
     assert d["value"] > 0 and d["unit"] == "GB/s" and d["higher_is_better"] is True
     assert d["vs_baseline"] is None and d["data"] == "synthetic" and d["cpu_baseline"] is None
-    assert d["cpu_baseline_all_cores"] is None and d["hot"] is None
+    assert d["cpu_baseline_all_cores"] is None and d["hot"] is None and d["overlap_2streams"] is None
     m = d["device_memory"]
     assert m is not None and m["memory_bus_width_bits"] > 0 and m["memory_clock_khz"] > 0
     c = d["copy_calibration"]
@@ -98,3 +98,19 @@ def test_json_line(gpu, op):
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert "traffic" in r and 0 < r["frac"] < 1 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("op", ["share", "strided", "all_shares", "quantize"])
+def test_overlap_context(gpu, op):
+    """--overlap adds a context figure and leaves the rest of the line as it is."""
+    wl = "w4_bs4096_h4096_e4m3_bf16"
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--op", op, "--workload", wl, "--steps",
+                          "20", "--warmup", "10", "--no-cpu-baseline", "--overlap"], capture_output=True, text=True,
+                         timeout=240)
+    assert res.returncode == 0, res.stderr[-2000:]
+    d = json.loads([ln for ln in res.stdout.splitlines() if ln.strip()][0])
+    o = d["overlap_2streams"]
+    assert o["us_per_step"] > 0 and o["sets_per_stream"] >= 1
+    assert abs(o["GBps"] - d["config"]["algorithmic_bytes_per_step"] / o["us_per_step"] / 1e3) < 0.01 * o["GBps"]
+    assert d["value"] > 0 and d["roofline"]["kernel_us_avg"] > 0

@@ -235,6 +235,30 @@ def test_prepared_launch_matches_run(gpu):
     assert_parity(out_bits(o2), want, wl.out_dtype, "Launch")
 
 
+def test_launch_on_another_stream(gpu):
+    """Launch.on_stream enqueues the same share on the given stream: the
+    output appears there (after that stream's earlier work) with the bits of
+    the original launch."""
+    import quantized_collective_reduction_amd as qrs
+
+    wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"].with_(bs=8 * 21)
+    xs, ss = workloads.generate(wl)
+    p = qrs.plan(8, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    dx, ds = to_device(xs, ss)
+    o1 = empty_out(wl.rows, wl.h, wl.out_dtype)
+    launch = qrs.Launch(p, dx, ds, o1)
+    launch()
+    s = torch.cuda.Stream()
+    side = launch.on_stream(s)
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o1.view(torch.int16).fill_(-1)  # ordered before the side launch on the same stream
+    side()
+    s.synchronize()
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype), wl.out_dtype)
+    assert_parity(out_bits(o1), want, wl.out_dtype, "Launch.on_stream")
+
+
 @pytest.mark.parametrize("x_format,scale_layout", [("e4m3fn", "e8m0_block32"), ("e5m2", "f32_group128"),
                                                    ("int8", "f32_group128")])
 def test_typed_float8_tensors(gpu, x_format, scale_layout):
