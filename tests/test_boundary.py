@@ -424,3 +424,32 @@ def test_last_error_cleared_by_a_successful_call(lib):
     assert lib.qrs_plan(2, 16, 1024, 1, 1, 1, ctypes.byref(handle), ctypes.byref(ws)) == qrs.Status.OK
     assert lib.qrs_last_error().decode() == ""
     lib.qrs_plan_destroy(handle)
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """Without the built libqrs.so the binding raises at its first call: there
+    is no CPU fallback for any entry point. Checked on a copy of the package
+    without the library, in a fresh interpreter."""
+    import shutil
+    import subprocess
+    import sys
+
+    pkg = os.path.dirname(os.path.abspath(qrs.__file__))
+    dst = tmp_path / "quantized_collective_reduction_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    assert not list(dst.glob("*.so"))
+    code = (
+        "import quantized_collective_reduction_amd as q\n"
+        "for call in (lambda: q.plan(8, 64, 1024, 'e4m3fn', 'e8m0_block32', 'bf16'),\n"
+        "             lambda: q.load_library()):\n"
+        "    try:\n"
+        "        call()\n"
+        "    except ImportError as e:\n"
+        "        assert 'no CPU fallback' in str(e), e\n"
+        "    else:\n"
+        "        raise SystemExit('no error without the library')\n"
+        "print('ok')\n"
+    )
+    res = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True, timeout=120,
+                         env={**os.environ, "PYTHONPATH": str(tmp_path)})
+    assert res.returncode == 0 and res.stdout.strip() == "ok", res.stderr[-2000:]
