@@ -103,7 +103,8 @@ def fp32_to_f16_bits(acc):
     above 65504 (that is, |v| >= 65520) is infinity. NaN maps to a quiet NaN
     of the same sign.
     """
-    v = np.ascontiguousarray(acc, dtype=np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):  # signalling NaN patterns widen to quiet NaNs
+        v = np.ascontiguousarray(acc, dtype=np.float32).astype(np.float64)
     a = np.abs(v)
     with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
         _, e2 = np.frexp(a)  # a = m * 2^e2, m in [0.5, 1)

@@ -156,6 +156,7 @@ class Plan:
     """An immutable plan for one share shape and mode (phase 1 of the op)."""
 
     def __init__(self, world_size, bs, h, x_dtype, scale_layout, out_dtype):
+        self._handle = None  # set first: __del__ runs even when a check below raises
         lib = load_library()
         self.world_size = int(world_size)
         self.bs = int(bs)
@@ -165,7 +166,6 @@ class Plan:
         self.out_dtype = _enum(out_dtype, _OUT_NAMES, OutDtype)
         handle = ctypes.c_void_p()
         ws = ctypes.c_size_t()
-        self._handle = None
         _check(lib.qrs_plan(self.world_size, self.bs, self.h, int(self.x_dtype), int(self.scale_layout),
                             int(self.out_dtype), ctypes.byref(handle), ctypes.byref(ws)))
         self._handle = handle
@@ -183,7 +183,7 @@ class Plan:
         return 128 if self.scale_layout == ScaleLayout.F32_GROUP128 else 32
 
     def __del__(self):
-        if self._handle is not None and _lib is not None:
+        if getattr(self, "_handle", None) is not None and _lib is not None:
             _lib.qrs_plan_destroy(self._handle)
             self._handle = None
 

@@ -453,3 +453,23 @@ def test_missing_library_fails_loudly(tmp_path):
     res = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True, timeout=120,
                          env={**os.environ, "PYTHONPATH": str(tmp_path)})
     assert res.returncode == 0 and res.stdout.strip() == "ok", res.stderr[-2000:]
+
+
+def test_failed_plan_construction_leaves_nothing_to_clean_up(lib):
+    """A Plan whose arguments are rejected before the C call (an unknown
+    dtype name) is finalized without error: no exception escapes __del__."""
+    import gc
+    import sys
+
+    caught = []
+    old = sys.unraisablehook
+    sys.unraisablehook = caught.append
+    try:
+        with pytest.raises(ValueError):
+            qrs.plan(8, 64, 1024, "e4m3", "e8m0_block32", "bf16")
+        with pytest.raises(qrs.QrsError):
+            qrs.plan(3, 64, 1024, "e4m3fn", "e8m0_block32", "bf16")
+        gc.collect()
+    finally:
+        sys.unraisablehook = old
+    assert not caught, [str(c.exc_value) for c in caught]
