@@ -132,7 +132,7 @@ def cpu_baseline(wl, xs, ss, min_seconds=10.0, min_reps=3):
 
 
 def _host_threads():
-    """Host cores this process may use, at most 16 (a GPU machine's CPU share)."""
+    """Host cores this process may use, at most 16 (the host CPU share of one GPU)."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
