@@ -28,6 +28,14 @@ inline hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, arg_ptrs, 0, stream);
 }
 
+// The same with `lds` bytes of dynamic LDS per block.
+template <typename... Params>
+inline hipError_t launch_kernel_lds(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
+                                    typename same_type<Params>::type... args) {
+  void* arg_ptrs[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, arg_ptrs, lds, stream);
+}
+
 // Element and scale formats as the kernels see them.
 enum XFormat : int { kXInt8 = 0, kXE4M3FN = 1, kXE5M2 = 2 };
 enum ScaleLayout : int { kScaleF32Group128 = 0, kScaleE8M0Block32 = 1 };
