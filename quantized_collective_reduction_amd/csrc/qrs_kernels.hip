@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "qrs_launch.h"
 
 // The definition has one rounding per product and per sum: never fuse.
@@ -552,21 +554,25 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
 }
 
 // Dynamic LDS, never touched by the kernel, that leaves room for only
-// QRS_FLAT_BLOCKS_PER_CU blocks of Kernel per CU; 0 for grids under three
-// generations of such blocks. One instantiation (and one cached static LDS
-// size) per kernel.
+// QRS_FLAT_BLOCKS_PER_CU blocks of Kernel per CU (gfx950: 256 CUs, 160 KiB
+// of LDS each); 0 for grids under three generations of such blocks. One
+// instantiation, and one cached static LDS size, per kernel. If the size
+// cannot be read, the launch runs uncapped and the next one asks again.
 template <auto Kernel>
 size_t flat_cap_lds(uint64_t blocks) {
   constexpr size_t kLdsPerCu = 160 * 1024;
   constexpr uint64_t kCus = 256;
   if (QRS_FLAT_BLOCKS_PER_CU <= 0 || blocks < 3 * kCus * QRS_FLAT_BLOCKS_PER_CU) return 0;
-  static const size_t static_lds = [] {
+  static std::atomic<int64_t> cached_static_lds{-1};
+  int64_t static_lds = cached_static_lds.load(std::memory_order_relaxed);
+  if (static_lds < 0) {
     hipFuncAttributes attr;
-    return hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(Kernel)) == hipSuccess ? attr.sharedSizeBytes
-                                                                                            : size_t{0};
-  }();
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(Kernel)) != hipSuccess) return 0;
+    static_lds = static_cast<int64_t>(attr.sharedSizeBytes);
+    cached_static_lds.store(static_lds, std::memory_order_relaxed);
+  }
   const size_t per_block = kLdsPerCu / QRS_FLAT_BLOCKS_PER_CU;
-  return per_block > static_lds ? per_block - static_lds : 0;
+  return per_block > static_cast<size_t>(static_lds) ? per_block - static_cast<size_t>(static_lds) : 0;
 }
 
 template <int W, int XF, int SL, int OF>
