@@ -11,6 +11,7 @@ import quantized_collective_reduction_amd as qrs
 import workloads
 from gpu_util import assert_parity, empty_out, oracle_bits, out_bits
 from oracle.quantize import quantize as oracle_quantize
+from test_oracle_quantize_examples import AMAX_COL, V_COL, example_input, load_examples
 
 pytestmark = pytest.mark.gpu
 
@@ -151,3 +152,17 @@ def test_producer_to_reduce_scatter_pipeline(gpu, x_format, scale_layout, out_dt
         got = outs[j].float().cpu().numpy().astype(np.float64)
         mag = sum(np.abs(b) for b in blocks)
         assert np.all(np.abs(got - exact) <= bound + out_rel * np.abs(got) + w * 2.0 ** -23 * (mag + bound))
+
+
+@pytest.mark.parametrize("ex", load_examples(), ids=lambda e: e["name"])
+def test_hand_derived_group_examples(gpu, ex):
+    """The hand-derived midpoint groups of tests/golden/quantize_examples.json
+    through the kernel: the code of v, of amax and the group's scale."""
+    bits = np.repeat(example_input(ex), 3, axis=0)
+    gc, gs = _gpu_quantize(bits, ex["x_format"], "f32_group128")
+    qmax_code = {"int8": 0x7F, "e4m3fn": 0x7E, "e5m2": 0x7B}[ex["x_format"]]
+    assert np.all(gc[:, V_COL] == int(ex["expected_code"], 16)), (ex["name"], hex(int(gc[0, V_COL])))
+    assert np.all(gc[:, AMAX_COL] == qmax_code)
+    assert np.all(gs[:, 0] == int(ex["expected_scale_bits"], 16))
+    wc, ws = _want(bits, ex["x_format"], "f32_group128")
+    assert np.array_equal(gc, wc) and np.array_equal(gs, ws)
