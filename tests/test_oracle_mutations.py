@@ -144,3 +144,32 @@ def test_planted_decode_mistakes_are_caught():
     assert not _decode_pin_passes(e5m2_bias16, "e5m2", torch.float8_e5m2)
     assert not _decode_pin_passes(e4m3_no_subnormals, "e4m3fn", torch.float8_e4m3fn)
     assert not _decode_pin_passes(int8_unsigned, "int8", torch.int8)
+
+
+ORDER_MUTANTS = ("reverse_rank_order", "pairwise_tree_sum")
+
+
+def test_other_orders_stated_by_the_examples():
+    """The bits each fold-order example states for the other orders are what
+    those orders compute."""
+    checked = 0
+    for ex in load_worked_examples():
+        for name, bits in ex.get("other_orders", {}).items():
+            xs, ss = build_example(ex)
+            out = _fold(xs, ss, ex["x_format"], ex["scale_layout"], ex["out_dtype"], **MUTANTS[name])
+            got = out.view(np.uint32) if ex["out_dtype"] == "f32" else out
+            assert np.all(got == int(bits, 16)), (ex["name"], name, hex(int(got.ravel()[0])))
+            checked += 1
+    assert checked >= 6
+
+
+@pytest.mark.parametrize("name", ORDER_MUTANTS)
+def test_each_order_mutant_is_rejected_by_two_examples(name):
+    rejected = []
+    for ex in load_worked_examples():
+        xs, ss = build_example(ex)
+        out = _fold(xs, ss, ex["x_format"], ex["scale_layout"], ex["out_dtype"], **MUTANTS[name])
+        got = out.view(np.uint32) if ex["out_dtype"] == "f32" else out
+        if not np.all(got == int(ex["expected_bits"], 16)):
+            rejected.append(ex["name"])
+    assert len(rejected) >= 2, (name, rejected)
