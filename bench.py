@@ -2,7 +2,7 @@
 reduce-scatter (dequant + rank-ordered reduce) on MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--op OP] [--layout L]
-                    [--hot] [--no-cpu-baseline] [--gpus 1]
+                    [--hot] [--overlap] [--no-cpu-baseline] [--no-largest] [--gpus 1]
 
 A step is one launch of the whole hot path (decode, scale, rank-ordered fp32
 fold, convert, store) over one batch: W rank slices of the workload, already
@@ -42,6 +42,14 @@ Prints ONE JSON line on stdout:
                    over two streams of the default priority (independent
                    batches, each stream on its own rotating sets), wall
                    time per step; else null.
+  largest_workload with --op share (the default), unless --no-largest: the
+                   largest workload (W=8, BS=65536, H=5120, MX E5M2 -> fp32)
+                   timed the same way in the same run, after the headline
+                   workload's buffers are freed (W warm-up launches, K timed
+                   launches between HIP events, wall clock around them):
+                   kernel_us_avg, achieved GB/s and frac of the 8 TB/s peak,
+                   and its whole-run GB/s; no CPU leg. Null when the
+                   headline workload is itself that one.
 Diagnostics go to stderr.
 """
 
@@ -328,6 +336,59 @@ def setup_quantize(wl, dev, qrs, workloads, torch, layout):
 OPS = {"share": setup_share, "strided": setup_strided, "all_shares": setup_all_shares, "quantize": setup_quantize}
 
 
+LARGEST = "w8_bs65536_h5120_mx_e5m2_f32"
+
+
+def time_steps(launches, warmup, steps, stream, torch):
+    """W untimed launches, then K timed ones rotating over the sets: HIP
+    events on the launch stream at both ends, wall clock around them (with a
+    synchronize on both sides). Returns (wall seconds, seconds per launch)."""
+    n_sets = len(launches)
+    for i in range(warmup):
+        launches[i % n_sets]()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    order = [launches[(warmup + i) % n_sets] for i in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for launch in order:
+        launch()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, ev0.elapsed_time(ev1) / 1e3 / steps
+
+
+def time_largest(args, dev, qrs, workloads, torch):
+    """The largest workload's share, timed like the headline steps."""
+    wl = workloads.WORKLOADS[LARGEST]
+    log(f"[bench] largest workload {wl.name}: W={wl.world_size} BS={wl.bs} H={wl.h} rows={wl.rows}")
+    alg_bytes, launches, outs, _ = setup_share(wl, dev, qrs, workloads, torch, args.layout)
+    stream = torch.cuda.current_stream(dev)
+    torch.cuda.synchronize()
+    wall, per_launch = time_steps(launches, args.warmup, args.steps, stream, torch)
+    achieved = alg_bytes / per_launch / 1e9
+    log(f"[bench] largest workload: {args.steps} steps in {wall * 1e3:.2f} ms wall; HIP events: "
+        f"{per_launch * 1e6:.2f} us per launch = {achieved:.0f} GB/s")
+    del launches, outs
+    torch.cuda.empty_cache()
+    return {
+        "workload": f"{wl.name}: W={wl.world_size} BS={wl.bs} H={wl.h} x={wl.x_format} scales={wl.scale_layout} "
+                    f"out={wl.out_dtype}",
+        "algorithmic_bytes_per_step": alg_bytes,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "kernel_us_avg": round(per_launch * 1e6, 3),
+        "achieved": round(achieved, 2),
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBPS, 4),
+        "value": round(alg_bytes * args.steps / wall / 1e9, 2),
+        "ms_per_step": round(wall * 1e3 / args.steps, 6),
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,6 +410,8 @@ def main():
                     help="also time K launches on one input/output set, without rotation (context only)")
     ap.add_argument("--overlap", action="store_true",
                     help="also time K independent steps alternated over two streams (context only)")
+    ap.add_argument("--no-largest", action="store_true",
+                    help="skip the largest workload's extra timing (largest_workload = null)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -379,30 +442,17 @@ def main():
     log(f"[bench] {alg_bytes} algorithmic bytes per step; {n_sets} rotating input/output sets on "
         f"{torch.cuda.get_device_name(dev)}")
 
-    for i in range(args.warmup):
-        launches[i % n_sets]()
-    torch.cuda.synchronize()
-    # All sets hold identical inputs, so every set must produce the same bits.
-    if args.warmup >= n_sets:
+    # Timed region: K back-to-back launches after W warm-up ones, HIP events
+    # on the launch stream at both ends, wall clock around it.
+    wall, avg_launch_s = time_steps(launches, args.warmup, args.steps, stream, torch)
+    # All sets hold identical inputs, so every set that ran must hold the same bits.
+    if args.warmup + args.steps >= n_sets:
         for o in outs[1:]:
             for a, b in zip(o, outs[0]):
                 if not torch.equal(a.view(torch.uint8), b.view(torch.uint8)):
                     sys.exit("rotating sets disagree: the kernel is not deterministic")
-
-    # Timed region: K back-to-back launches, HIP events on the launch stream
-    # at both ends, wall clock around it.
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
-    order = [launches[(args.warmup + i) % n_sets] for i in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for launch in order:
-        launch()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    avg_launch_s = ev0.elapsed_time(ev1) / 1e3 / args.steps
     log(f"[bench] {args.steps} steps in {wall * 1e3:.2f} ms wall; HIP events over the region: "
         f"{avg_launch_s * 1e6:.2f} us per launch")
 
@@ -469,6 +519,12 @@ def main():
     log(f"[bench] stream-copy calibration: {2 * copy_bytes} bytes moved in {copy_s * 1e6:.2f} us = {copy_gbps:.0f} GB/s")
     del src, dst, copies
 
+    largest = None
+    if args.op == "share" and not args.no_largest and wl.name != LARGEST:
+        del launches, outs
+        torch.cuda.empty_cache()
+        largest = time_largest(args, dev, qrs, workloads, torch)
+
     achieved = alg_bytes / avg_launch_s / 1e9
     value = alg_bytes * args.steps / wall / 1e9
     result = {
@@ -500,6 +556,12 @@ def main():
             "h": wl.h,
             "algorithmic_bytes_per_step": alg_bytes,
             "rotating_sets": n_sets,
+            # dtype above is the arithmetic type (the fp32 products and fold);
+            # these are the element types the step reads and writes.
+            "element_types": {"x": wl.x_format, "scales": {"f32_group128": "f32", "e8m0_block32": "e8m0"}[wl.scale_layout],
+                              "out": wl.out_dtype} if args.op != "quantize" else
+                             {"in": "bf16", "codes": wl.x_format,
+                              "scales": {"f32_group128": "f32", "e8m0_block32": "e8m0"}[wl.scale_layout]},
         },
         "pct_of_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "roofline": {
@@ -515,6 +577,7 @@ def main():
         "copy_calibration": {"bytes_moved": 2 * copy_bytes, "us": round(copy_s * 1e6, 3),
                              "GBps": round(copy_gbps, 1)},
         "overlap_2streams": overlap,
+        "largest_workload": largest,
         "hot": None if hot_s is None else {
             "kernel_us_avg": round(hot_s * 1e6, 3), "GBps": round(alg_bytes / hot_s / 1e9, 2),
             "note": "context only: one input/output set, no rotation"},

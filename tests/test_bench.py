@@ -78,7 +78,8 @@ def test_oracle_row_blocks_concatenate_to_the_whole_share(name):
 def test_json_line(gpu, op):
     wl = "w4_bs4096_h4096_e4m3_bf16"
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--op", op, "--workload", wl, "--steps",
-                          "20", "--warmup", "10", "--no-cpu-baseline"], capture_output=True, text=True, timeout=240)
+                          "20", "--warmup", "10", "--no-cpu-baseline", "--no-largest"], capture_output=True, text=True,
+                         timeout=240)
     assert res.returncode == 0, res.stderr[-2000:]
     lines = [ln for ln in res.stdout.splitlines() if ln.strip()]
     assert len(lines) == 1, "exactly one line on stdout"
@@ -98,6 +99,28 @@ def test_json_line(gpu, op):
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == 8000.0
     assert "traffic" in r and 0 < r["frac"] < 1 and abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    assert d["largest_workload"] is None
+    assert d["dtype"] == "f32" and set(d["config"]["element_types"]) >= {"scales"}
+
+
+@pytest.mark.gpu
+def test_largest_workload_is_timed_beside_the_headline(gpu):
+    """The default share run also times the largest workload (W=8,
+    BS=65536, H=5120) and reports it under its own key."""
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "w4_bs4096_h4096_e4m3_bf16",
+                          "--steps", "20", "--warmup", "5", "--no-cpu-baseline"], capture_output=True, text=True,
+                         timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    d = json.loads([ln for ln in res.stdout.splitlines() if ln.strip()][0])
+    big = d["largest_workload"]
+    wl = workloads.WORKLOADS[bench.LARGEST]
+    assert big["workload"].startswith(bench.LARGEST)
+    assert big["algorithmic_bytes_per_step"] == wl.algorithmic_bytes() and big["steps"] == 20
+    assert big["kernel_us_avg"] > 0 and big["unit"] == "GB/s"
+    assert abs(big["achieved"] - big["algorithmic_bytes_per_step"] / big["kernel_us_avg"] / 1e3) < 1e-3 * big["achieved"]
+    assert abs(big["frac"] - big["achieved"] / 8000.0) < 1e-3 and 0 < big["frac"] < 1
+    assert 0 < big["value"] <= big["achieved"] * 1.001
+    assert d["config"]["workload"].startswith("w4_bs4096_h4096_e4m3_bf16")
 
 
 @pytest.mark.gpu
@@ -106,7 +129,8 @@ def test_overlap_context(gpu, op):
     """--overlap adds a context figure and leaves the rest of the line as it is."""
     wl = "w4_bs4096_h4096_e4m3_bf16"
     res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--op", op, "--workload", wl, "--steps",
-                          "20", "--warmup", "10", "--no-cpu-baseline", "--overlap"], capture_output=True, text=True,
+                          "20", "--warmup", "10", "--no-cpu-baseline", "--overlap", "--no-largest"], capture_output=True,
+                         text=True,
                          timeout=240)
     assert res.returncode == 0, res.stderr[-2000:]
     d = json.loads([ln for ln in res.stdout.splitlines() if ln.strip()][0])
