@@ -281,6 +281,37 @@ qrs_status qrs_plan_shape(qrs_plan_t plan, int64_t* rows_out, int64_t* h_out);
  */
 qrs_status qrs_slice_pitch(qrs_plan_t plan, int full_inputs, size_t* x_pitch_out, size_t* scale_pitch_out);
 
+/*
+ * The launch qrs_run makes for this plan on the device of `stream` (a
+ * hipStream_t; NULL = the current device), reported without launching
+ * anything. Host only; the library reads the device's sizes with
+ * hipDeviceGetAttribute (once per device) but enqueues no work.
+ *
+ *   blocks             work-groups in the grid;
+ *   threads_per_block  threads per work-group;
+ *   dynamic_lds_bytes  unused LDS requested per work-group so that at most
+ *                      blocks_per_cu_cap work-groups reside on one CU (large
+ *                      contiguous shares only; 0 = no cap);
+ *   blocks_per_cu_cap  that cap (0 = none);
+ *   device_cus, device_lds_per_cu, device_lds_per_block
+ *                      the device sizes the cap is derived from (CU count,
+ *                      LDS bytes per CU, LDS bytes one work-group may use);
+ *                      0 if they could not be read (then no cap).
+ *
+ * Returns QRS_ERR_INVALID_ARG for a null plan or info pointer.
+ */
+typedef struct qrs_launch_info {
+  uint64_t blocks;
+  uint32_t threads_per_block;
+  uint32_t dynamic_lds_bytes;
+  uint32_t blocks_per_cu_cap;
+  uint32_t device_cus;
+  uint32_t device_lds_per_cu;
+  uint32_t device_lds_per_block;
+} qrs_launch_info;
+
+qrs_status qrs_run_launch_info(qrs_plan_t plan, void* stream, qrs_launch_info* info_out);
+
 /* Static, never-null name of a status code. */
 const char* qrs_status_string(qrs_status status);
 

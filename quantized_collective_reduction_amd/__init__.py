@@ -40,6 +40,8 @@ __all__ = [
     "AllSharesLaunch",
     "QuantizeLaunch",
     "stream_copy",
+    "run_launch_info",
+    "LaunchInfo",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -87,7 +89,25 @@ EXPORTED_SYMBOLS = (
     "qrs_status_string",
     "qrs_last_error",
     "qrs_stream_copy",
+    "qrs_run_launch_info",
 )
+
+
+class LaunchInfo(ctypes.Structure):
+    """qrs_launch_info: the launch qrs_run makes for a plan (see run_launch_info)."""
+
+    _fields_ = [
+        ("blocks", ctypes.c_uint64),
+        ("threads_per_block", ctypes.c_uint32),
+        ("dynamic_lds_bytes", ctypes.c_uint32),
+        ("blocks_per_cu_cap", ctypes.c_uint32),
+        ("device_cus", ctypes.c_uint32),
+        ("device_lds_per_cu", ctypes.c_uint32),
+        ("device_lds_per_block", ctypes.c_uint32),
+    ]
+
+    def as_dict(self):
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
 
 
 class QrsError(RuntimeError):
@@ -133,6 +153,8 @@ def load_library(path: str = LIB_PATH):
     lib.qrs_last_error.restype = ctypes.c_char_p
     lib.qrs_stream_copy.argtypes = [vp, vp, c_sz, vp]
     lib.qrs_stream_copy.restype = c_int
+    lib.qrs_run_launch_info.argtypes = [vp, vp, ctypes.POINTER(LaunchInfo)]
+    lib.qrs_run_launch_info.restype = c_int
     _lib = lib
     return lib
 
@@ -527,6 +549,15 @@ class QuantizeLaunch:
         status = self._fn(*self._args)
         if status:
             _check(status)
+
+
+def run_launch_info(p: Plan, stream=None) -> dict:
+    """The grid, residency cap and device sizes of the launch ``run`` makes
+    for ``p`` on ``stream``'s device (qrs_run_launch_info); launches nothing."""
+    lib = load_library()
+    info = LaunchInfo()
+    _check(lib.qrs_run_launch_info(p.handle, _stream_handle(stream), ctypes.byref(info)))
+    return info.as_dict()
 
 
 def stream_copy(src, dst, nbytes=None, stream=None):

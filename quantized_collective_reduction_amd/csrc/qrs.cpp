@@ -197,6 +197,30 @@ qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* con
   return ok();
 }
 
+qrs_status qrs_run_launch_info(qrs_plan_t plan, void* stream, qrs_launch_info* info_out) {
+  if (!plan || !info_out) return fail(QRS_ERR_INVALID_ARG, "null plan or info pointer");
+  qrs::ReduceLaunch l;
+  std::memset(&l, 0, sizeof(l));
+  l.world_size = plan->world_size;
+  l.x_format = plan->x_format;
+  l.scale_layout = plan->scale_layout;
+  l.out_format = plan->out_format;
+  l.n_rows = 1;
+  l.row_elems = static_cast<uint64_t>(plan->rows) * static_cast<uint64_t>(plan->h);
+  l.n_shares = 1;
+  qrs::LaunchShape shape;
+  const hipError_t e = qrs::reduce_launch_shape(l, static_cast<hipStream_t>(stream), &shape);
+  if (e != hipSuccess) return fail(QRS_ERR_HIP, "launch shape: %s", hipGetErrorString(e));
+  info_out->blocks = shape.blocks;
+  info_out->threads_per_block = shape.threads_per_block;
+  info_out->dynamic_lds_bytes = shape.dynamic_lds;
+  info_out->blocks_per_cu_cap = shape.blocks_per_cu_cap;
+  info_out->device_cus = shape.device.cus;
+  info_out->device_lds_per_cu = shape.device.lds_per_cu;
+  info_out->device_lds_per_block = shape.device.lds_per_block;
+  return ok();
+}
+
 qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const void* const* scale_full,
                               void* const* out_shares, void* workspace, size_t workspace_bytes, void* stream) {
   (void)workspace;

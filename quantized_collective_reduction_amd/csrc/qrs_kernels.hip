@@ -92,8 +92,9 @@
 // resident per CU (0 = no cap). Fewer waves in flight keep the HBM request
 // queues shorter; measured faster on every such share shape tried (0.3-8 %),
 // and slower on smaller grids, row-strided shares and all-shares launches,
-// which stay uncapped. The cap is unused dynamic LDS (160 KiB per CU on
-// gfx950, divided among the blocks).
+// which stay uncapped. The cap is unused dynamic LDS: the launch device's
+// LDS per CU (160 KiB on gfx950) divided among the blocks, with the CU count
+// and LDS sizes read from the device.
 #ifndef QRS_FLAT_BLOCKS_PER_CU
 #define QRS_FLAT_BLOCKS_PER_CU 4
 #endif
@@ -553,31 +554,58 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
   }
 }
 
-// Dynamic LDS, never touched by the kernel, that leaves room for only
-// QRS_FLAT_BLOCKS_PER_CU blocks of Kernel per CU (gfx950: 256 CUs, 160 KiB
-// of LDS each); 0 for grids under three generations of such blocks. One
-// instantiation, and one cached static LDS size, per kernel. If the size
-// cannot be read, the launch runs uncapped and the next one asks again.
+// One launch, chosen but not yet enqueued: the kernel instantiation, its
+// grid, the dynamic LDS that caps residency, and the launch device's sizes
+// (zeros when they were not read).
+struct Prepared {
+  const void* kernel = nullptr;
+  dim3 grid;
+  dim3 block;
+  size_t lds = 0;
+  uint32_t blocks_per_cu_cap = 0;
+  DeviceShape device{};
+  KernelArgs args;
+};
+
+hipError_t launch_prepared(const Prepared& p, hipStream_t stream) {
+  KernelArgs a = p.args;
+  void* arg_ptrs[] = {&a};
+  return hipLaunchKernel(p.kernel, p.grid, p.block, arg_ptrs, p.lds, stream);
+}
+
+// Unused dynamic LDS that leaves room for only QRS_FLAT_BLOCKS_PER_CU blocks
+// of Kernel per CU of the launch device. No cap for grids under three
+// generations of such blocks, when the device's sizes or the kernel's static
+// LDS cannot be read (the next launch asks again), or when one block may not
+// allocate its share. One instantiation, and one cached static LDS size, per
+// kernel.
 template <auto Kernel>
-size_t flat_cap_lds(uint64_t blocks) {
-  constexpr size_t kLdsPerCu = 160 * 1024;
-  constexpr uint64_t kCus = 256;
-  if (QRS_FLAT_BLOCKS_PER_CU <= 0 || blocks < 3 * kCus * QRS_FLAT_BLOCKS_PER_CU) return 0;
+void flat_cap(uint64_t blocks, hipStream_t stream, Prepared* p) {
+  constexpr uint64_t N = QRS_FLAT_BLOCKS_PER_CU;
+  // No device has fewer than 32 CUs per partition here: smaller grids are
+  // never capped, and skip the device query.
+  if (N == 0 || blocks < 3 * 32 * N) return;
+  DeviceShape d;
+  if (!device_shape(stream, &d)) return;
+  p->device = d;
+  if (blocks < 3 * static_cast<uint64_t>(d.cus) * N) return;
   static std::atomic<int64_t> cached_static_lds{-1};
   int64_t static_lds = cached_static_lds.load(std::memory_order_relaxed);
   if (static_lds < 0) {
     hipFuncAttributes attr;
-    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(Kernel)) != hipSuccess) return 0;
+    if (hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(Kernel)) != hipSuccess) return;
     static_lds = static_cast<int64_t>(attr.sharedSizeBytes);
     cached_static_lds.store(static_lds, std::memory_order_relaxed);
   }
-  const size_t per_block = kLdsPerCu / QRS_FLAT_BLOCKS_PER_CU;
-  return per_block > static_cast<size_t>(static_lds) ? per_block - static_cast<size_t>(static_lds) : 0;
+  const uint64_t per_block = d.lds_per_cu / N;
+  if (per_block > d.lds_per_block || per_block <= static_cast<uint64_t>(static_lds)) return;
+  p->lds = per_block - static_cast<uint64_t>(static_lds);
+  p->blocks_per_cu_cap = static_cast<uint32_t>(N);
 }
 
 template <int W, int XF, int SL, int OF>
-hipError_t launch_typed(const ReduceLaunch& l, hipStream_t stream) {
-  KernelArgs a;
+hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p) {
+  KernelArgs& a = p->args;
   for (int r = 0; r < kMaxWorld; ++r) {
     a.x[r] = r < W ? static_cast<const u32x4*>(l.x[r]) : nullptr;
     a.scales[r] = r < W ? l.scales[r] : nullptr;
@@ -614,49 +642,72 @@ hipError_t launch_typed(const ReduceLaunch& l, hipStream_t stream) {
   a.out_row_stride = static_cast<uint32_t>(l.out_row_stride / 16);
   a.x_share_stride = l.x_share_stride / 16;
   a.scale_share_stride = l.scale_share_stride;
-  const dim3 grid(static_cast<uint32_t>(blocks), l.n_shares);
-  const dim3 block(QRS_BLOCK);
+  p->grid = dim3(static_cast<uint32_t>(blocks), l.n_shares);
+  p->block = dim3(QRS_BLOCK);
   if (l.n_shares > 1) {
     if (l.n_rows != 1) return hipErrorInvalidValue;
-    return launch_kernel(reduce_kernel<W, XF, SL, OF, kAddrShares>, grid, block, stream, a);
+    p->kernel = reinterpret_cast<const void*>(reduce_kernel<W, XF, SL, OF, kAddrShares>);
+    return hipSuccess;
   }
-  if (l.n_rows > 1) return launch_kernel(reduce_kernel<W, XF, SL, OF, kAddrRows>, grid, block, stream, a);
+  if (l.n_rows > 1) {
+    p->kernel = reinterpret_cast<const void*>(reduce_kernel<W, XF, SL, OF, kAddrRows>);
+    return hipSuccess;
+  }
   // The output is the largest of the share's tensors (at least 2 bytes per
   // element against 1 + 1/32 for a slice and its scales).
   if (a.chunks_per_row * OutPieces<OF>::kCount * sizeof(u32x4) < (1ull << 32)) {
     constexpr auto kernel = reduce_kernel<W, XF, SL, OF, kAddrFlat32>;
-    return launch_kernel_lds(kernel, grid, block, flat_cap_lds<kernel>(blocks), stream, a);
+    p->kernel = reinterpret_cast<const void*>(kernel);
+    flat_cap<kernel>(blocks, stream, p);
+    return hipSuccess;
   }
   constexpr auto kernel = reduce_kernel<W, XF, SL, OF, kAddrFlat>;
-  return launch_kernel_lds(kernel, grid, block, flat_cap_lds<kernel>(blocks), stream, a);
+  p->kernel = reinterpret_cast<const void*>(kernel);
+  flat_cap<kernel>(blocks, stream, p);
+  return hipSuccess;
 }
 
 template <int W, int XF, int SL>
-hipError_t dispatch_out(const ReduceLaunch& l, hipStream_t s) {
+hipError_t prepare_out(const ReduceLaunch& l, hipStream_t s, Prepared* p) {
   switch (l.out_format) {
-    case kOutF32: return launch_typed<W, XF, SL, kOutF32>(l, s);
-    case kOutBF16: return launch_typed<W, XF, SL, kOutBF16>(l, s);
-    case kOutF16: return launch_typed<W, XF, SL, kOutF16>(l, s);
+    case kOutF32: return prepare_typed<W, XF, SL, kOutF32>(l, s, p);
+    case kOutBF16: return prepare_typed<W, XF, SL, kOutBF16>(l, s, p);
+    case kOutF16: return prepare_typed<W, XF, SL, kOutF16>(l, s, p);
   }
   return hipErrorInvalidValue;
 }
 
 template <int W>
-hipError_t dispatch_mode(const ReduceLaunch& l, hipStream_t s) {
+hipError_t prepare_mode(const ReduceLaunch& l, hipStream_t s, Prepared* p) {
   if (l.scale_layout == kScaleE8M0Block32) {
     switch (l.x_format) {
-      case kXE4M3FN: return dispatch_out<W, kXE4M3FN, kScaleE8M0Block32>(l, s);
-      case kXE5M2: return dispatch_out<W, kXE5M2, kScaleE8M0Block32>(l, s);
+      case kXE4M3FN: return prepare_out<W, kXE4M3FN, kScaleE8M0Block32>(l, s, p);
+      case kXE5M2: return prepare_out<W, kXE5M2, kScaleE8M0Block32>(l, s, p);
       default: return hipErrorInvalidValue;  // INT8 has no MX mode
     }
   }
   switch (l.x_format) {
-    case kXInt8: return dispatch_out<W, kXInt8, kScaleF32Group128>(l, s);
-    case kXE4M3FN: return dispatch_out<W, kXE4M3FN, kScaleF32Group128>(l, s);
-    case kXE5M2: return dispatch_out<W, kXE5M2, kScaleF32Group128>(l, s);
+    case kXInt8: return prepare_out<W, kXInt8, kScaleF32Group128>(l, s, p);
+    case kXE4M3FN: return prepare_out<W, kXE4M3FN, kScaleF32Group128>(l, s, p);
+    case kXE5M2: return prepare_out<W, kXE5M2, kScaleF32Group128>(l, s, p);
   }
   return hipErrorInvalidValue;
 }
+
+hipError_t prepare_reduce(const ReduceLaunch& l, hipStream_t stream, Prepared* p) {
+  switch (l.world_size) {
+    case 2: return prepare_mode<2>(l, stream, p);
+    case 4: return prepare_mode<4>(l, stream, p);
+    case 8: return prepare_mode<8>(l, stream, p);
+  }
+  return hipErrorInvalidValue;
+}
+
+// Launch devices whose sizes are cached (device ordinal below this).
+constexpr int kMaxDevices = 64;
+// Per device: CUs in bits 0-15, LDS per CU in bits 16-39, LDS per block in
+// bits 40-63; 0 until read.
+std::atomic<uint64_t> g_device_shape[kMaxDevices];
 
 __global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
                                                           uint64_t n) {
@@ -666,13 +717,50 @@ __global__ __launch_bounds__(256) void stream_copy_kernel(const u32x4* __restric
 
 }  // namespace
 
-hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream) {
-  switch (l.world_size) {
-    case 2: return dispatch_mode<2>(l, stream);
-    case 4: return dispatch_mode<4>(l, stream);
-    case 8: return dispatch_mode<8>(l, stream);
+bool device_shape(hipStream_t stream, DeviceShape* out) {
+  int dev = -1;
+  if (stream != nullptr) {
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess) return false;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    return false;
   }
-  return hipErrorInvalidValue;
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  uint64_t packed = g_device_shape[dev].load(std::memory_order_relaxed);
+  if (packed == 0) {
+    int cus = 0, lds_cu = 0, lds_block = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&lds_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      return false;
+    if (cus <= 0 || cus > 0xFFFF || lds_cu <= 0 || lds_cu > 0xFFFFFF || lds_block <= 0 || lds_block > 0xFFFFFF)
+      return false;
+    packed = static_cast<uint64_t>(cus) | static_cast<uint64_t>(lds_cu) << 16 | static_cast<uint64_t>(lds_block) << 40;
+    g_device_shape[dev].store(packed, std::memory_order_relaxed);
+  }
+  out->cus = static_cast<uint32_t>(packed & 0xFFFF);
+  out->lds_per_cu = static_cast<uint32_t>((packed >> 16) & 0xFFFFFF);
+  out->lds_per_block = static_cast<uint32_t>(packed >> 40);
+  return true;
+}
+
+hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream) {
+  Prepared p;
+  const hipError_t e = prepare_reduce(l, stream, &p);
+  if (e != hipSuccess) return e;
+  return launch_prepared(p, stream);
+}
+
+hipError_t reduce_launch_shape(const ReduceLaunch& l, hipStream_t stream, LaunchShape* out) {
+  Prepared p;
+  const hipError_t e = prepare_reduce(l, stream, &p);
+  if (e != hipSuccess) return e;
+  out->blocks = static_cast<uint64_t>(p.grid.x) * p.grid.y * p.grid.z;
+  out->threads_per_block = p.block.x * p.block.y * p.block.z;
+  out->dynamic_lds = static_cast<uint32_t>(p.lds);
+  out->blocks_per_cu_cap = p.blocks_per_cu_cap;
+  out->device = p.device;
+  if (out->device.cus == 0 && !device_shape(stream, &out->device)) out->device = DeviceShape{};
+  return hipSuccess;
 }
 
 hipError_t launch_stream_copy(const void* src, void* dst, uint64_t bytes, hipStream_t stream) {

@@ -28,14 +28,6 @@ inline hipError_t launch_kernel(void (*kernel)(Params...), dim3 grid, dim3 block
   return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, arg_ptrs, 0, stream);
 }
 
-// The same with `lds` bytes of dynamic LDS per block.
-template <typename... Params>
-inline hipError_t launch_kernel_lds(void (*kernel)(Params...), dim3 grid, dim3 block, size_t lds, hipStream_t stream,
-                                    typename same_type<Params>::type... args) {
-  void* arg_ptrs[] = {static_cast<void*>(&args)...};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, arg_ptrs, lds, stream);
-}
-
 // Element and scale formats as the kernels see them.
 enum XFormat : int { kXInt8 = 0, kXE4M3FN = 1, kXE5M2 = 2 };
 enum ScaleLayout : int { kScaleF32Group128 = 0, kScaleE8M0Block32 = 1 };
@@ -79,6 +71,31 @@ struct ReduceLaunch {
 // a scale slice spanning 4 GiB or more, or a row of fewer than 64 or more
 // than 768 chunks.
 hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream);
+
+// The launch device's compute-unit count and LDS sizes in bytes, as
+// hipDeviceGetAttribute reports them (multiprocessor count, shared memory per
+// multiprocessor, shared memory per block) for the device of `stream` (the
+// current device for the null stream). Read once per device and cached;
+// false if they cannot be read.
+struct DeviceShape {
+  uint32_t cus;
+  uint32_t lds_per_cu;
+  uint32_t lds_per_block;
+};
+bool device_shape(hipStream_t stream, DeviceShape* out);
+
+// What launch_reduce would enqueue for l on stream, without enqueuing it:
+// work-groups, threads per work-group, the unused dynamic LDS that caps
+// residency (0 = none), the cap in work-groups per CU (0 = none), and the
+// device sizes the cap was derived from (zeros if they could not be read).
+struct LaunchShape {
+  uint64_t blocks;
+  uint32_t threads_per_block;
+  uint32_t dynamic_lds;
+  uint32_t blocks_per_cu_cap;
+  DeviceShape device;
+};
+hipError_t reduce_launch_shape(const ReduceLaunch& l, hipStream_t stream, LaunchShape* out);
 
 // Producer-side quantization of n_elems bf16 values (a multiple of 128,
 // row-major [tokens, H] with G dividing H, so groups never cross rows):

@@ -114,6 +114,13 @@ def test_destroy_null_and_shape_of_null(lib):
     assert lib.qrs_plan_shape(None, None, None) == qrs.Status.INVALID_ARG
 
 
+def test_launch_info_rejects_null_arguments(lib):
+    info = qrs.LaunchInfo()
+    assert lib.qrs_run_launch_info(None, None, ctypes.byref(info)) == qrs.Status.INVALID_ARG
+    p = qrs.plan(8, 16384, 8192, "e4m3fn", "e8m0_block32", "bf16")
+    assert lib.qrs_run_launch_info(p.handle, None, None) == qrs.Status.INVALID_ARG
+
+
 # qrs_run checks its arguments on the host before it touches the GPU; these
 # calls return before any HIP call.
 

@@ -1,0 +1,90 @@
+"""The residency cap of large contiguous shares comes from the launch
+device's own sizes: qrs_run_launch_info reports the CU count and LDS sizes
+the library read, and they must be the ones the HIP runtime reports for the
+device; the cap must follow from them."""
+
+import ctypes
+
+import pytest
+import torch
+
+import quantized_collective_reduction_amd as qrs
+
+pytestmark = pytest.mark.gpu
+
+# hipDeviceAttribute_t values (hip_runtime_api.h, ROCm 7)
+ATTR_MULTIPROCESSOR_COUNT = 63
+ATTR_MAX_SHARED_MEMORY_PER_MULTIPROCESSOR = 10002
+ATTR_MAX_SHARED_MEMORY_PER_BLOCK = 74
+BLOCKS_PER_CU = 4  # the library's cap for large contiguous shares
+
+
+def _hip_attr(attr, dev=0):
+    path = None
+    with open("/proc/self/maps") as f:
+        for line in f:
+            if "libamdhip64.so" in line:
+                path = line.split()[-1]
+                break
+    assert path is not None, "the HIP runtime is not loaded"
+    hip = ctypes.CDLL(path)
+    v = ctypes.c_int(0)
+    assert hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev) == 0
+    return v.value
+
+
+def _static_lds(info):
+    # dynamic = lds_per_cu / cap - static
+    return info["device_lds_per_cu"] // info["blocks_per_cu_cap"] - info["dynamic_lds_bytes"]
+
+
+def test_device_sizes_are_the_runtimes(gpu):
+    torch.zeros(1, device="cuda")  # the runtime is initialised
+    p = qrs.plan(8, 16384, 8192, "e4m3fn", "e8m0_block32", "bf16")
+    info = qrs.run_launch_info(p)
+    assert info["device_cus"] == _hip_attr(ATTR_MULTIPROCESSOR_COUNT)
+    assert info["device_cus"] == torch.cuda.get_device_properties(0).multi_processor_count
+    assert info["device_lds_per_cu"] == _hip_attr(ATTR_MAX_SHARED_MEMORY_PER_MULTIPROCESSOR)
+    assert info["device_lds_per_block"] == _hip_attr(ATTR_MAX_SHARED_MEMORY_PER_BLOCK)
+
+
+@pytest.mark.parametrize("w,bs,h,xd,sl,od", [
+    (8, 16384, 8192, "e4m3fn", "e8m0_block32", "bf16"),   # 4096 blocks
+    (8, 65536, 5120, "e5m2", "e8m0_block32", "f32"),      # 10240 blocks, fp32 staging in LDS
+    (2, 8192, 8192, "int8", "f32_group128", "f32"),       # 8192 blocks
+])
+def test_cap_follows_from_the_device(gpu, w, bs, h, xd, sl, od):
+    p = qrs.plan(w, bs, h, xd, sl, od)
+    info = qrs.run_launch_info(p)
+    cus = info["device_cus"]
+    assert info["threads_per_block"] == 256
+    assert info["blocks"] == p.rows * h // 16 // 256
+    if info["blocks"] >= 3 * cus * BLOCKS_PER_CU:
+        assert info["blocks_per_cu_cap"] == BLOCKS_PER_CU
+        per_block = info["device_lds_per_cu"] // BLOCKS_PER_CU
+        assert per_block <= info["device_lds_per_block"]
+        static = _static_lds(info)
+        if od == "f32":
+            assert static == 16 * 1024  # the fp32 outputs' staging buffer
+        else:
+            assert static < 1024
+        assert info["dynamic_lds_bytes"] == per_block - static
+    else:
+        assert info["blocks_per_cu_cap"] == 0 and info["dynamic_lds_bytes"] == 0
+
+
+@pytest.mark.parametrize("w,bs,h,xd,sl,od", [
+    (8, 8192, 7168, "e5m2", "f32_group128", "bf16"),   # 1792 blocks: one generation, uncapped
+    (2, 32, 1024, "int8", "f32_group128", "f32"),      # 4 blocks
+])
+def test_small_grids_are_not_capped(gpu, w, bs, h, xd, sl, od):
+    p = qrs.plan(w, bs, h, xd, sl, od)
+    info = qrs.run_launch_info(p)
+    assert info["blocks"] < 3 * info["device_cus"] * BLOCKS_PER_CU
+    assert info["blocks_per_cu_cap"] == 0 and info["dynamic_lds_bytes"] == 0
+
+
+def test_launch_info_on_a_side_stream(gpu):
+    s = torch.cuda.Stream()
+    p = qrs.plan(8, 16384, 8192, "e4m3fn", "e8m0_block32", "bf16")
+    assert qrs.run_launch_info(p, stream=s) == qrs.run_launch_info(p)
