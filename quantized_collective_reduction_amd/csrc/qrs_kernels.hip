@@ -25,8 +25,10 @@
 // and scale in one scaled conversion instead (exact, see product_pair).
 // fp32 outputs go through LDS and 16-bit outputs with fp32 group scales
 // through a cross-half lane swap, so that each store instruction writes one
-// contiguous 1 KiB. Which variant each mode uses was chosen by measurement;
-// the macros below select them.
+// contiguous 1 KiB. MX modes with 16-bit outputs get the same from lanes
+// that own 8 elements (a "piece": one 8-byte load per rank, one 16-byte
+// store) in the contiguous share. Which variant each mode uses was chosen by
+// measurement; the macros below select them.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -84,6 +86,19 @@
 #ifndef QRS_MX_SCALED_CVT
 #define QRS_MX_SCALED_CVT 1
 #endif
+// MX scales with 16-bit outputs: lanes own 8-element pieces instead of
+// 16-element chunks in the contiguous share, so that each lane's output is
+// one 16-byte store and every store instruction of a wave writes one
+// contiguous 1 KiB (no partial lines reach HBM). 1: on (measured faster at
+// W = 2, 4 and 8 with its own residency cap, below); 0: chunks as above.
+#ifndef QRS_MX16_PIECES
+#define QRS_MX16_PIECES 1
+#endif
+// The piece kernel's blocks, renumbered so that the two that share each
+// line of scales run on one XCD (see reduce_piece_kernel). 1: on; 0: off.
+#ifndef QRS_PIECE_XCD_PAIRS
+#define QRS_PIECE_XCD_PAIRS 1
+#endif
 // 1: block barrier around the LDS exchange; 0: wave-local ordering only.
 #ifndef QRS_STAGE_BLOCK_SYNC
 #define QRS_STAGE_BLOCK_SYNC 0
@@ -103,6 +118,7 @@ namespace qrs {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
@@ -554,6 +570,130 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
   }
 }
 
+// acc[0..7] = rank-ordered fold of the dequantized products of one
+// 8-element piece (decode, then one rounded multiply and one rounded add per
+// rank, as in fold_chunk).
+template <int W, int XF>
+__device__ __forceinline__ void fold_piece(const u32x2 (&xv)[W], const float (&sv)[W], float (&acc)[8]) {
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const uint32_t w = xv[0][q];
+    const f32x2 lo = decode_pair<XF>(w, false);
+    const f32x2 hi = decode_pair<XF>(w, true);
+    acc[4 * q + 0] = lo.x * sv[0];
+    acc[4 * q + 1] = lo.y * sv[0];
+    acc[4 * q + 2] = hi.x * sv[0];
+    acc[4 * q + 3] = hi.y * sv[0];
+  }
+#pragma unroll
+  for (int r = 1; r < W; ++r) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t w = xv[r][q];
+      const f32x2 lo = decode_pair<XF>(w, false);
+      const f32x2 hi = decode_pair<XF>(w, true);
+      const float p0 = lo.x * sv[r];
+      const float p1 = lo.y * sv[r];
+      const float p2 = hi.x * sv[r];
+      const float p3 = hi.y * sv[r];
+      acc[4 * q + 0] = acc[4 * q + 0] + p0;
+      acc[4 * q + 1] = acc[4 * q + 1] + p1;
+      acc[4 * q + 2] = acc[4 * q + 2] + p2;
+      acc[4 * q + 3] = acc[4 * q + 3] + p3;
+    }
+  }
+}
+
+// The contiguous share with MX scales and a 16-bit output: lane l of block b
+// owns piece p = b * QRS_BLOCK + l, elements [8p, 8p + 8). It loads 8 code
+// bytes per rank (one 8-byte load; a wave's load covers 512 contiguous
+// bytes) and the piece's E8M0 byte (element 8p's block of 32, byte p / 4),
+// folds, converts to 8 16-bit values and writes them with one 16-byte store,
+// so a wave's store covers 1 KiB contiguously. SHARES = false: one share,
+// every slice, scale slice and the output under 4 GiB (32-bit offsets on the
+// scalar bases). SHARES = true: all W shares of contiguous pre-all-to-all
+// inputs, share j = blockIdx.y reading row block j of every rank (64-bit
+// offsets) and writing out[j].
+template <int W, int XF, int OF, bool SHARES>
+__global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
+  static_assert(OF != kOutF32 && XF != kXInt8, "MX scales with a 16-bit output");
+  const uint64_t n_pieces = a.chunks_per_row * 2;
+  uint32_t b = blockIdx.x;
+#if QRS_PIECE_XCD_PAIRS
+  // A block covers 64 E8M0 bytes per rank, half a 128-byte line, so two
+  // consecutive blocks share every scale line. The hardware hands block ids
+  // to the XCDs in turn (linear id mod 8), so ids b and b + 8 run on one
+  // XCD: within each full group of 16 ids, id 16g + 8h + x takes the pieces
+  // of block 16g + 2x + h, and each scale line is fetched into one L2.
+  if (b < (gridDim.x & ~15u)) b = (b & ~15u) | ((b & 7u) << 1) | ((b >> 3) & 1u);
+#endif
+  const uint64_t p = static_cast<uint64_t>(b) * QRS_BLOCK + threadIdx.x;
+  if (p >= n_pieces) return;
+  u32x2 xv[W];
+  float sv[W];
+  void* out_base;
+  if constexpr (SHARES) {
+    const uint32_t share = blockIdx.y;
+    const uint64_t xb = share * a.x_share_stride * sizeof(u32x4) + p * 8u;
+    const uint64_t sb = share * a.scale_share_stride + (p >> 2);
+#pragma unroll
+    for (int r = 0; r < W; ++r)
+      xv[r] = load_stream(reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(a.x[r]) + xb));
+#pragma unroll
+    for (int r = 0; r < W; ++r) sv[r] = decode_e8m0(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
+    out_base = a.out[share];
+  } else {
+    const uint32_t xb = static_cast<uint32_t>(p) * 8u;
+    const uint32_t sb = static_cast<uint32_t>(p >> 2);
+#pragma unroll
+    for (int r = 0; r < W; ++r)
+      xv[r] = load_stream(reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(a.x[r]) + xb));
+#pragma unroll
+    for (int r = 0; r < W; ++r) sv[r] = decode_e8m0(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
+    out_base = a.out[0];
+  }
+  float acc[8];
+  fold_piece<W, XF>(xv, sv, acc);
+  uint32_t packed[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    f32x2 pr;
+    pr.x = acc[2 * k];
+    pr.y = acc[2 * k + 1];
+    if constexpr (OF == kOutBF16)
+      packed[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));  // RNE
+    else
+      packed[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, f16x2));  // RNE
+  }
+  const u32x4 v = {packed[0], packed[1], packed[2], packed[3]};
+  if constexpr (SHARES)
+    store_stream(static_cast<u32x4*>(out_base) + p, v);
+  else
+    store_stream(reinterpret_cast<u32x4*>(static_cast<char*>(out_base) + static_cast<uint32_t>(p) * 16u), v);
+}
+
+// Whether a kernel instantiation takes the piece layout.
+template <int SL, int OF>
+constexpr bool kPieceLayout = QRS_MX16_PIECES && SL == kScaleE8M0Block32 && OF != kOutF32;
+
+// Blocks resident per CU for the piece kernel (0 = no cap), by world size.
+// A lane keeps W 8-byte loads in flight: at W = 8 six blocks per CU
+// measured best (W=8 shares with H = 8192 and 5120; 4 and 5 slower), at
+// W = 2 and 4 full occupancy (capped at 4 or 6 blocks they ran 0-16 %
+// slower).
+#ifndef QRS_PIECE_BLOCKS_PER_CU_W8
+#define QRS_PIECE_BLOCKS_PER_CU_W8 6
+#endif
+#ifndef QRS_PIECE_BLOCKS_PER_CU_W4
+#define QRS_PIECE_BLOCKS_PER_CU_W4 0
+#endif
+#ifndef QRS_PIECE_BLOCKS_PER_CU_W2
+#define QRS_PIECE_BLOCKS_PER_CU_W2 0
+#endif
+template <int W>
+constexpr uint32_t kPieceBlocksPerCu =
+    W >= 8 ? QRS_PIECE_BLOCKS_PER_CU_W8 : (W >= 4 ? QRS_PIECE_BLOCKS_PER_CU_W4 : QRS_PIECE_BLOCKS_PER_CU_W2);
+
 // One launch, chosen but not yet enqueued: the kernel instantiation, its
 // grid, the dynamic LDS that caps residency, and the launch device's sizes
 // (zeros when they were not read).
@@ -573,15 +713,14 @@ hipError_t launch_prepared(const Prepared& p, hipStream_t stream) {
   return hipLaunchKernel(p.kernel, p.grid, p.block, arg_ptrs, p.lds, stream);
 }
 
-// Unused dynamic LDS that leaves room for only QRS_FLAT_BLOCKS_PER_CU blocks
-// of Kernel per CU of the launch device. No cap for grids under three
+// Unused dynamic LDS that leaves room for only N blocks of Kernel per CU of
+// the launch device. No cap for grids under three
 // generations of such blocks, when the device's sizes or the kernel's static
 // LDS cannot be read (the next launch asks again), or when one block may not
 // allocate its share. One instantiation, and one cached static LDS size, per
 // kernel.
 template <auto Kernel>
-void flat_cap(uint64_t blocks, hipStream_t stream, Prepared* p) {
-  constexpr uint64_t N = QRS_FLAT_BLOCKS_PER_CU;
+void flat_cap(uint64_t blocks, uint64_t N, hipStream_t stream, Prepared* p) {
   // No device has fewer than 32 CUs per partition here: smaller grids are
   // never capped, and skip the device query.
   if (N == 0 || blocks < 3 * 32 * N) return;
@@ -644,8 +783,15 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
   a.scale_share_stride = l.scale_share_stride;
   p->grid = dim3(static_cast<uint32_t>(blocks), l.n_shares);
   p->block = dim3(QRS_BLOCK);
+  const uint64_t piece_blocks = (a.chunks_per_row * 2 + QRS_BLOCK - 1) / QRS_BLOCK;
   if (l.n_shares > 1) {
     if (l.n_rows != 1) return hipErrorInvalidValue;
+    if constexpr (kPieceLayout<SL, OF>) {
+      if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+      p->grid = dim3(static_cast<uint32_t>(piece_blocks), l.n_shares);
+      p->kernel = reinterpret_cast<const void*>(reduce_piece_kernel<W, XF, OF, true>);
+      return hipSuccess;
+    }
     p->kernel = reinterpret_cast<const void*>(reduce_kernel<W, XF, SL, OF, kAddrShares>);
     return hipSuccess;
   }
@@ -656,14 +802,22 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
   // The output is the largest of the share's tensors (at least 2 bytes per
   // element against 1 + 1/32 for a slice and its scales).
   if (a.chunks_per_row * OutPieces<OF>::kCount * sizeof(u32x4) < (1ull << 32)) {
+    if constexpr (kPieceLayout<SL, OF>) {
+      if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+      constexpr auto kernel = reduce_piece_kernel<W, XF, OF, false>;
+      p->grid = dim3(static_cast<uint32_t>(piece_blocks));
+      p->kernel = reinterpret_cast<const void*>(kernel);
+      flat_cap<kernel>(piece_blocks, kPieceBlocksPerCu<W>, stream, p);
+      return hipSuccess;
+    }
     constexpr auto kernel = reduce_kernel<W, XF, SL, OF, kAddrFlat32>;
     p->kernel = reinterpret_cast<const void*>(kernel);
-    flat_cap<kernel>(blocks, stream, p);
+    flat_cap<kernel>(blocks, QRS_FLAT_BLOCKS_PER_CU, stream, p);
     return hipSuccess;
   }
   constexpr auto kernel = reduce_kernel<W, XF, SL, OF, kAddrFlat>;
   p->kernel = reinterpret_cast<const void*>(kernel);
-  flat_cap<kernel>(blocks, stream, p);
+  flat_cap<kernel>(blocks, QRS_FLAT_BLOCKS_PER_CU, stream, p);
   return hipSuccess;
 }
 

@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 ATTR_MULTIPROCESSOR_COUNT = 63
 ATTR_MAX_SHARED_MEMORY_PER_MULTIPROCESSOR = 10002
 ATTR_MAX_SHARED_MEMORY_PER_BLOCK = 74
-BLOCKS_PER_CU = 4  # the library's cap for large contiguous shares
+BLOCKS_PER_CU = 4  # the library's cap for large contiguous shares of 16-element chunks
+PIECE_BLOCKS_PER_CU_W8 = 6  # ... and of 8-element pieces (MX scales, 16-bit output) at W = 8
 
 
 def _hip_attr(attr, dev=0):
@@ -38,6 +39,7 @@ def _static_lds(info):
     return info["device_lds_per_cu"] // info["blocks_per_cu_cap"] - info["dynamic_lds_bytes"]
 
 
+
 def test_device_sizes_are_the_runtimes(gpu):
     torch.zeros(1, device="cuda")  # the runtime is initialised
     p = qrs.plan(8, 16384, 8192, "e4m3fn", "e8m0_block32", "bf16")
@@ -48,20 +50,34 @@ def test_device_sizes_are_the_runtimes(gpu):
     assert info["device_lds_per_block"] == _hip_attr(ATTR_MAX_SHARED_MEMORY_PER_BLOCK)
 
 
+def _expected_layout(w, sl, od):
+    """Elements per lane and blocks per CU of the contiguous share: MX scales
+    with a 16-bit output take 8-element pieces, capped at 6 blocks per CU
+    at W = 8 and uncapped below; every other mode 16-element chunks capped
+    at 4."""
+    if sl == "e8m0_block32" and od != "f32":
+        return 8, (PIECE_BLOCKS_PER_CU_W8 if w == 8 else 0)
+    return 16, BLOCKS_PER_CU
+
+
 @pytest.mark.parametrize("w,bs,h,xd,sl,od", [
-    (8, 16384, 8192, "e4m3fn", "e8m0_block32", "bf16"),   # 4096 blocks
+    (8, 16384, 8192, "e4m3fn", "e8m0_block32", "bf16"),   # 8192 piece blocks
+    (8, 16384, 8192, "e5m2", "e8m0_block32", "f16"),      # 8192 piece blocks
+    (4, 8192, 8192, "e4m3fn", "e8m0_block32", "bf16"),    # 8192 piece blocks, uncapped at W = 4
     (8, 65536, 5120, "e5m2", "e8m0_block32", "f32"),      # 10240 blocks, fp32 staging in LDS
     (2, 8192, 8192, "int8", "f32_group128", "f32"),       # 8192 blocks
+    (8, 16384, 8192, "e4m3fn", "f32_group128", "bf16"),   # 4096 blocks
 ])
 def test_cap_follows_from_the_device(gpu, w, bs, h, xd, sl, od):
     p = qrs.plan(w, bs, h, xd, sl, od)
     info = qrs.run_launch_info(p)
     cus = info["device_cus"]
+    per_lane, n_cap = _expected_layout(w, sl, od)
     assert info["threads_per_block"] == 256
-    assert info["blocks"] == p.rows * h // 16 // 256
-    if info["blocks"] >= 3 * cus * BLOCKS_PER_CU:
-        assert info["blocks_per_cu_cap"] == BLOCKS_PER_CU
-        per_block = info["device_lds_per_cu"] // BLOCKS_PER_CU
+    assert info["blocks"] == -(-p.rows * h // per_lane // 256)
+    if n_cap and info["blocks"] >= 3 * cus * n_cap:
+        assert info["blocks_per_cu_cap"] == n_cap
+        per_block = info["device_lds_per_cu"] // n_cap
         assert per_block <= info["device_lds_per_block"]
         static = _static_lds(info)
         if od == "f32":

@@ -315,3 +315,30 @@ def test_recommended_slice_placement(gpu, full):
         torch.cuda.synchronize()
         want = oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype)
         assert_parity(out_bits(out), oracle_bits(want, wl.out_dtype), wl.out_dtype, "pitched")
+
+
+@pytest.mark.parametrize("x_format,scale_layout", [("e4m3fn", "e8m0_block32"), ("e5m2", "e8m0_block32"),
+                                                   ("int8", "f32_group128")])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("w,rows,h", [(8, 3, 1152), (4, 7, 1024), (2, 1, 8192)])
+def test_share_writes_only_its_output(gpu, x_format, scale_layout, out_dtype, w, rows, h):
+    """The output is the head of a larger buffer whose tail holds NaN: the
+    tail must survive (ragged element counts, every output type, the MX
+    16-bit piece layout included)."""
+    import quantized_collective_reduction_amd as qrs
+
+    wl = workloads.Workload("guard", w, rows * w, h, x_format, scale_layout, out_dtype,
+                            x_dist="int_uniform" if x_format == "int8" else "normal",
+                            x_param=127 if x_format == "int8" else 40,
+                            scale_lo=-10 if scale_layout == "f32_group128" else 110,
+                            scale_hi=2 if scale_layout == "f32_group128" else 140, seed=77 + w + rows)
+    xs, ss = workloads.generate(wl)
+    p = qrs.plan(w, rows * w, h, x_format, scale_layout, out_dtype)
+    dx, ds = to_device(xs, ss)
+    n = rows * h
+    big = empty_out(1, n + 4096, out_dtype).fill_(float("nan")).view(-1)
+    qrs.run(p, dx, ds, big[:n].view(rows, h))
+    torch.cuda.synchronize()
+    assert torch.isnan(big[n:].float()).all(), "the share wrote past its output"
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, x_format, scale_layout, out_dtype), out_dtype)
+    assert_parity(out_bits(big[:n].view(rows, h)), want, out_dtype, "guard")
