@@ -94,6 +94,11 @@
 #ifndef QRS_MX16_PIECES
 #define QRS_MX16_PIECES 1
 #endif
+// The chunk kernel's row-strided blocks, renumbered in pairs per XCD like
+// the piece kernel's (1) or in hardware order (0).
+#ifndef QRS_ROWS_XCD_PAIRS
+#define QRS_ROWS_XCD_PAIRS 0
+#endif
 // The piece kernel's blocks, renumbered so that the two that share each
 // line of scales run on one XCD (see reduce_piece_kernel). 1: on; 0: off.
 #ifndef QRS_PIECE_XCD_PAIRS
@@ -393,6 +398,13 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
 #if QRS_XCD_REMAP
   if ((gridDim.x & 7u) == 0) block_id = (block_id & 7u) * (gridDim.x >> 3) + (block_id >> 3);
 #endif
+#if QRS_ROWS_XCD_PAIRS
+  // Row-strided shares: scale rows need not start on a line, so consecutive
+  // blocks can share one; pair them on one XCD as the piece kernel does.
+  if constexpr (ROWS) {
+    if (block_id < (gridDim.x & ~15u)) block_id = (block_id & ~15u) | ((block_id & 7u) << 1) | ((block_id >> 3) & 1u);
+  }
+#endif
   // First chunk of this block (uniform). Chunk j of this lane is
   // base + j*QRS_BLOCK: every load instruction of a wave covers one
   // contiguous range of chunks (for row-strided shares, one contiguous range
@@ -604,20 +616,25 @@ __device__ __forceinline__ void fold_piece(const u32x2 (&xv)[W], const float (&s
   }
 }
 
-// The contiguous share with MX scales and a 16-bit output: lane l of block b
-// owns piece p = b * QRS_BLOCK + l, elements [8p, 8p + 8). It loads 8 code
-// bytes per rank (one 8-byte load; a wave's load covers 512 contiguous
-// bytes) and the piece's E8M0 byte (element 8p's block of 32, byte p / 4),
-// folds, converts to 8 16-bit values and writes them with one 16-byte store,
-// so a wave's store covers 1 KiB contiguously. SHARES = false: one share,
-// every slice, scale slice and the output under 4 GiB (32-bit offsets on the
-// scalar bases). SHARES = true: all W shares of contiguous pre-all-to-all
-// inputs, share j = blockIdx.y reading row block j of every rank (64-bit
-// offsets) and writing out[j].
-template <int W, int XF, int OF, bool SHARES>
+// Shares with MX scales and a 16-bit output: lane l of block b owns piece
+// p = b * QRS_BLOCK + l of the share, elements [8p, 8p + 8). It loads 8 code
+// bytes per rank (one 8-byte load; a wave's load covers 512 contiguous bytes
+// of a row) and the piece's E8M0 byte (element 8p's block of 32), folds,
+// converts to 8 16-bit values and writes them with one 16-byte store, so a
+// wave's store covers 1 KiB of a row contiguously. Addressing:
+//   kAddrFlat32  one contiguous share, every slice, scale slice and the
+//                output under 4 GiB (32-bit offsets on the scalar bases);
+//   kAddrShares  all W shares of contiguous pre-all-to-all inputs: share
+//                j = blockIdx.y reads row block j of every rank (64-bit
+//                offsets) and writes out[j];
+//   kAddrRows    one share with row-strided slices and output: piece p is
+//                column p mod (H / 8) of row p div (H / 8), the division a
+//                multiply by div_magic = ceil(2^64 / (H / 8)).
+template <int W, int XF, int OF, int ADDR>
 __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
   static_assert(OF != kOutF32 && XF != kXInt8, "MX scales with a 16-bit output");
-  const uint64_t n_pieces = a.chunks_per_row * 2;
+  static_assert(ADDR == kAddrFlat32 || ADDR == kAddrShares || ADDR == kAddrRows, "addressing");
+  const uint64_t n_pieces = a.total_chunks * 2;
   uint32_t b = blockIdx.x;
 #if QRS_PIECE_XCD_PAIRS
   // A block covers 64 E8M0 bytes per rank, half a 128-byte line, so two
@@ -631,8 +648,17 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
   if (p >= n_pieces) return;
   u32x2 xv[W];
   float sv[W];
-  void* out_base;
-  if constexpr (SHARES) {
+  u32x4* dst;
+  if constexpr (ADDR == kAddrFlat32) {
+    const uint32_t xb = static_cast<uint32_t>(p) * 8u;
+    const uint32_t sb = static_cast<uint32_t>(p >> 2);
+#pragma unroll
+    for (int r = 0; r < W; ++r)
+      xv[r] = load_stream(reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(a.x[r]) + xb));
+#pragma unroll
+    for (int r = 0; r < W; ++r) sv[r] = decode_e8m0(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
+    dst = reinterpret_cast<u32x4*>(static_cast<char*>(a.out[0]) + static_cast<uint32_t>(p) * 16u);
+  } else if constexpr (ADDR == kAddrShares) {
     const uint32_t share = blockIdx.y;
     const uint64_t xb = share * a.x_share_stride * sizeof(u32x4) + p * 8u;
     const uint64_t sb = share * a.scale_share_stride + (p >> 2);
@@ -641,16 +667,20 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
       xv[r] = load_stream(reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(a.x[r]) + xb));
 #pragma unroll
     for (int r = 0; r < W; ++r) sv[r] = decode_e8m0(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
-    out_base = a.out[share];
+    dst = static_cast<u32x4*>(a.out[share]) + p;
   } else {
-    const uint32_t xb = static_cast<uint32_t>(p) * 8u;
-    const uint32_t sb = static_cast<uint32_t>(p >> 2);
+    const uint64_t ppr = a.chunks_per_row * 2;  // pieces per row
+    const uint64_t row = __umul64hi(p, a.div_magic);
+    const uint32_t col = static_cast<uint32_t>(p - row * ppr);
+    const uint64_t xb = row * a.x_row_stride * sizeof(u32x4) + col * 8u;
+    // A scale slice spans less than 4 GiB (checked at launch).
+    const uint32_t sb = static_cast<uint32_t>(row) * a.scale_row_stride + (col >> 2);
 #pragma unroll
     for (int r = 0; r < W; ++r)
       xv[r] = load_stream(reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(a.x[r]) + xb));
 #pragma unroll
     for (int r = 0; r < W; ++r) sv[r] = decode_e8m0(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
-    out_base = a.out[0];
+    dst = static_cast<u32x4*>(a.out[0]) + row * a.out_row_stride + col;
   }
   float acc[8];
   fold_piece<W, XF>(xv, sv, acc);
@@ -665,11 +695,7 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
     else
       packed[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, f16x2));  // RNE
   }
-  const u32x4 v = {packed[0], packed[1], packed[2], packed[3]};
-  if constexpr (SHARES)
-    store_stream(static_cast<u32x4*>(out_base) + p, v);
-  else
-    store_stream(reinterpret_cast<u32x4*>(static_cast<char*>(out_base) + static_cast<uint32_t>(p) * 16u), v);
+  store_stream(dst, u32x4{packed[0], packed[1], packed[2], packed[3]});
 }
 
 // Whether a kernel instantiation takes the piece layout.
@@ -783,19 +809,26 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
   a.scale_share_stride = l.scale_share_stride;
   p->grid = dim3(static_cast<uint32_t>(blocks), l.n_shares);
   p->block = dim3(QRS_BLOCK);
-  const uint64_t piece_blocks = (a.chunks_per_row * 2 + QRS_BLOCK - 1) / QRS_BLOCK;
+  const uint64_t piece_blocks = (a.total_chunks * 2 + QRS_BLOCK - 1) / QRS_BLOCK;
   if (l.n_shares > 1) {
     if (l.n_rows != 1) return hipErrorInvalidValue;
     if constexpr (kPieceLayout<SL, OF>) {
       if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
       p->grid = dim3(static_cast<uint32_t>(piece_blocks), l.n_shares);
-      p->kernel = reinterpret_cast<const void*>(reduce_piece_kernel<W, XF, OF, true>);
+      p->kernel = reinterpret_cast<const void*>(reduce_piece_kernel<W, XF, OF, kAddrShares>);
       return hipSuccess;
     }
     p->kernel = reinterpret_cast<const void*>(reduce_kernel<W, XF, SL, OF, kAddrShares>);
     return hipSuccess;
   }
   if (l.n_rows > 1) {
+    if constexpr (kPieceLayout<SL, OF>) {
+      if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+      a.div_magic = ~0ull / (a.chunks_per_row * 2) + 1;  // rows of H / 8 pieces
+      p->grid = dim3(static_cast<uint32_t>(piece_blocks));
+      p->kernel = reinterpret_cast<const void*>(reduce_piece_kernel<W, XF, OF, kAddrRows>);
+      return hipSuccess;
+    }
     p->kernel = reinterpret_cast<const void*>(reduce_kernel<W, XF, SL, OF, kAddrRows>);
     return hipSuccess;
   }
@@ -804,7 +837,7 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
   if (a.chunks_per_row * OutPieces<OF>::kCount * sizeof(u32x4) < (1ull << 32)) {
     if constexpr (kPieceLayout<SL, OF>) {
       if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
-      constexpr auto kernel = reduce_piece_kernel<W, XF, OF, false>;
+      constexpr auto kernel = reduce_piece_kernel<W, XF, OF, kAddrFlat32>;
       p->grid = dim3(static_cast<uint32_t>(piece_blocks));
       p->kernel = reinterpret_cast<const void*>(kernel);
       flat_cap<kernel>(piece_blocks, kPieceBlocksPerCu<W>, stream, p);
