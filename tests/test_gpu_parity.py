@@ -342,3 +342,48 @@ def test_share_writes_only_its_output(gpu, x_format, scale_layout, out_dtype, w,
     assert torch.isnan(big[n:].float()).all(), "the share wrote past its output"
     want = oracle_bits(oracle.reduce_scatter_share(xs, ss, x_format, scale_layout, out_dtype), out_dtype)
     assert_parity(out_bits(big[:n].view(rows, h)), want, out_dtype, "guard")
+
+
+@pytest.mark.parametrize("w,rows,h", [
+    (8, 10, 8192),   # 40 piece blocks: 32 renumbered in pairs, 8 left in order
+    (8, 9, 8192),    # 36 blocks: 32 + 4
+    (4, 37, 1152),   # 21 blocks, the last one partial
+    (2, 64, 8192),   # 256 blocks, every one paired
+    (8, 31, 5120),   # 78 blocks, the last one partial
+])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+def test_piece_grids_with_unpaired_tails(gpu, w, rows, h, out_dtype):
+    """MX shares with 16-bit outputs run as 8-element pieces with blocks
+    renumbered in groups of 16: grids whose block count is not a multiple of
+    16 (and whose last block is partial) must still cover every element once,
+    through all three launch forms."""
+    import quantized_collective_reduction_amd as qrs
+
+    wl = workloads.Workload("tails", w, rows * w, h, "e4m3fn", "e8m0_block32", out_dtype, x_dist="normal",
+                            x_param=40, scale_lo=112, scale_hi=140, seed=4242 + rows)
+    xs, ss = workloads.generate(wl)
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, "e4m3fn", "e8m0_block32", out_dtype), out_dtype)
+    got = run_gpu(w, rows, h, "e4m3fn", "e8m0_block32", out_dtype, xs, ss)
+    assert_parity(got, want, out_dtype, "run")
+    # row-strided: each row padded by 256 elements
+    p = qrs.plan(w, rows * w, h, "e4m3fn", "e8m0_block32", out_dtype)
+    dx = [torch.zeros((rows, h + 256), dtype=torch.uint8, device="cuda") for _ in xs]
+    ds = [torch.zeros((rows, (h + 256) // 32), dtype=torch.uint8, device="cuda") for _ in ss]
+    for t, x in zip(dx, xs):
+        t[:, :h].copy_(torch.from_numpy(x))
+    for t, s in zip(ds, ss):
+        t[:, :h // 32].copy_(torch.from_numpy(s))
+    out_full = empty_out(rows, h + 256, out_dtype).fill_(float("nan"))
+    qrs.run_strided(p, [t[:, :h] for t in dx], [t[:, :h // 32] for t in ds], out_full[:, :h])
+    torch.cuda.synchronize()
+    assert_parity(out_bits(out_full[:, :h].contiguous()), want, out_dtype, "run_strided")
+    assert torch.isnan(out_full[:, h:].float()).all(), "run_strided wrote outside the output rows"
+    # all shares: each rank's full input is W copies of its slice's rows
+    xf = [np.concatenate([x] * w) for x in xs]
+    sf = [np.concatenate([s] * w) for s in ss]
+    fx, fs = to_device(xf, sf)
+    outs = [empty_out(rows, h, out_dtype).fill_(float("nan")) for _ in range(w)]
+    qrs.run_all_shares(p, fx, fs, outs)
+    torch.cuda.synchronize()
+    for j in range(w):
+        assert_parity(out_bits(outs[j]), want, out_dtype, f"all shares, share {j}")
