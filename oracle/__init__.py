@@ -24,6 +24,9 @@ Modules:
 * ``exact`` -- brute force with ``fractions.Fraction``: exact products and
   sums, each rounded to binary32 by a rounding routine written from the
   IEEE 754 definition. Used to pin ``reduce`` on tiny inputs.
+* ``quantize`` -- the producer side: bf16 activations to codes and scales,
+  MX by the OCP Microscaling conversion, per-token-per-group by one fp32
+  multiplier qmax / amax per group and one rounded product per element.
 
 Pins (tests marked "not gpu"): every decode table entry against torch's CPU
 float8 casts; bf16 rounding against torch's CPU cast; ``reduce`` against
@@ -31,7 +34,13 @@ float8 casts; bf16 rounding against torch's CPU cast; ``reduce`` against
 (exact integer sums under power-of-two scales, rank-permutation invariance
 where every partial sum is exact, single-rank identity, cancellation of
 opposite ranks, the recursive-summation error bound); hand-derived worked
-examples that fix the fold order and the absence of fused multiply-add.
+examples that fix the fold order (three orders told apart by two W = 4
+cases) and the absence of fused multiply-add. ``quantize``: its fp8 encoder
+against torch's casts and a brute-force nearest-code search, INT8 against
+round-half-even, re-quantizing quantized MX blocks, hand-derived shared
+exponents, zero and tiny groups, a round-trip error bound, and hand-derived
+per-group cases at rounding midpoints that fix the multiplier reading
+against dividing by the stored scale or multiplying by its reciprocal.
 """
 
 from .decode import (
