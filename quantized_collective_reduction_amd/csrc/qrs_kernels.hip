@@ -263,6 +263,10 @@ struct KernelArgs {
   uint32_t out_row_stride;    // in 16-byte units
   uint64_t x_share_stride;      // in 16-byte units
   uint64_t scale_share_stride;  // in bytes
+  // Piece kernels: block ids below this (the grid's full groups of 16) are
+  // renumbered in XCD pairs. Read from the arguments, with the rest of
+  // them, rather than from the dispatch packet.
+  uint32_t pair_limit;
 };
 
 // Orders a wave's LDS writes before its following LDS reads of other lanes'
@@ -616,6 +620,34 @@ __device__ __forceinline__ void fold_piece(const u32x2 (&xv)[W], const float (&s
   }
 }
 
+// Uses every argument the contiguous piece kernel reads (no instruction is
+// emitted), so that their scalar loads issue together at the start of a
+// wave and it waits once for them, instead of once for the bounds and
+// again, after the bounds check, for the base pointers (measured about 1 %
+// faster on the W=8 H=8192 share, whose waves are short-lived). One asm
+// statement per group: separate statements let the scheduler put a wait
+// between them.
+template <int W>
+__device__ __forceinline__ void pin_flat_args(const KernelArgs& a);
+template <>
+__device__ __forceinline__ void pin_flat_args<8>(const KernelArgs& a) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.x[2]), "s"(a.x[3]), "s"(a.x[4]), "s"(a.x[5]), "s"(a.x[6]),
+               "s"(a.x[7]));
+  asm volatile("" ::"s"(a.scales[0]), "s"(a.scales[1]), "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.scales[4]),
+               "s"(a.scales[5]), "s"(a.scales[6]), "s"(a.scales[7]), "s"(a.out[0]), "s"(a.total_chunks),
+               "s"(a.pair_limit));
+}
+template <>
+__device__ __forceinline__ void pin_flat_args<4>(const KernelArgs& a) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.x[2]), "s"(a.x[3]), "s"(a.scales[0]), "s"(a.scales[1]),
+               "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.out[0]), "s"(a.total_chunks), "s"(a.pair_limit));
+}
+template <>
+__device__ __forceinline__ void pin_flat_args<2>(const KernelArgs& a) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.scales[0]), "s"(a.scales[1]), "s"(a.out[0]),
+               "s"(a.total_chunks), "s"(a.pair_limit));
+}
+
 // Shares with MX scales and a 16-bit output: lane l of block b owns piece
 // p = b * QRS_BLOCK + l of the share, elements [8p, 8p + 8). It loads 8 code
 // bytes per rank (one 8-byte load; a wave's load covers 512 contiguous bytes
@@ -634,15 +666,17 @@ template <int W, int XF, int OF, int ADDR>
 __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
   static_assert(OF != kOutF32 && XF != kXInt8, "MX scales with a 16-bit output");
   static_assert(ADDR == kAddrFlat32 || ADDR == kAddrShares || ADDR == kAddrRows, "addressing");
+  if constexpr (ADDR == kAddrFlat32) pin_flat_args<W>(a);
   const uint64_t n_pieces = a.total_chunks * 2;
   uint32_t b = blockIdx.x;
 #if QRS_PIECE_XCD_PAIRS
   // A block covers 64 E8M0 bytes per rank, half a 128-byte line, so two
   // consecutive blocks share every scale line. The hardware hands block ids
   // to the XCDs in turn (linear id mod 8), so ids b and b + 8 run on one
-  // XCD: within each full group of 16 ids, id 16g + 8h + x takes the pieces
-  // of block 16g + 2x + h, and each scale line is fetched into one L2.
-  if (b < (gridDim.x & ~15u)) b = (b & ~15u) | ((b & 7u) << 1) | ((b >> 3) & 1u);
+  // XCD: within each full group of 16 ids (below pair_limit), id
+  // 16g + 8h + x takes the pieces of block 16g + 2x + h, and each scale
+  // line is fetched into one L2.
+  if (b < a.pair_limit) b = (b & ~15u) | ((b & 7u) << 1) | ((b >> 3) & 1u);
 #endif
   const uint64_t p = static_cast<uint64_t>(b) * QRS_BLOCK + threadIdx.x;
   if (p >= n_pieces) return;
@@ -650,14 +684,16 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
   float sv[W];
   u32x4* dst;
   if constexpr (ADDR == kAddrFlat32) {
-    const uint32_t xb = static_cast<uint32_t>(p) * 8u;
-    const uint32_t sb = static_cast<uint32_t>(p >> 2);
+    // 32-bit offsets on the scalar bases for the codes and the scale bytes.
+    const uint32_t p32 = static_cast<uint32_t>(p);
+    const uint32_t xb = p32 * 8u;
+    const uint32_t sb = p32 >> 2;
 #pragma unroll
     for (int r = 0; r < W; ++r)
       xv[r] = load_stream(reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(a.x[r]) + xb));
 #pragma unroll
     for (int r = 0; r < W; ++r) sv[r] = decode_e8m0(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
-    dst = reinterpret_cast<u32x4*>(static_cast<char*>(a.out[0]) + static_cast<uint32_t>(p) * 16u);
+    dst = reinterpret_cast<u32x4*>(static_cast<char*>(a.out[0]) + p32 * 16u);
   } else if constexpr (ADDR == kAddrShares) {
     const uint32_t share = blockIdx.y;
     const uint64_t xb = share * a.x_share_stride * sizeof(u32x4) + p * 8u;
@@ -730,7 +766,7 @@ struct Prepared {
   size_t lds = 0;
   uint32_t blocks_per_cu_cap = 0;
   DeviceShape device{};
-  KernelArgs args;
+  KernelArgs args{};
 };
 
 hipError_t launch_prepared(const Prepared& p, hipStream_t stream) {
@@ -815,6 +851,7 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
     if constexpr (kPieceLayout<SL, OF>) {
       if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
       p->grid = dim3(static_cast<uint32_t>(piece_blocks), l.n_shares);
+      a.pair_limit = static_cast<uint32_t>(piece_blocks) & ~15u;
       p->kernel = reinterpret_cast<const void*>(reduce_piece_kernel<W, XF, OF, kAddrShares>);
       return hipSuccess;
     }
@@ -826,6 +863,7 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
       if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
       a.div_magic = ~0ull / (a.chunks_per_row * 2) + 1;  // rows of H / 8 pieces
       p->grid = dim3(static_cast<uint32_t>(piece_blocks));
+      a.pair_limit = static_cast<uint32_t>(piece_blocks) & ~15u;
       p->kernel = reinterpret_cast<const void*>(reduce_piece_kernel<W, XF, OF, kAddrRows>);
       return hipSuccess;
     }
@@ -839,6 +877,7 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
       if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
       constexpr auto kernel = reduce_piece_kernel<W, XF, OF, kAddrFlat32>;
       p->grid = dim3(static_cast<uint32_t>(piece_blocks));
+      a.pair_limit = static_cast<uint32_t>(piece_blocks) & ~15u;
       p->kernel = reinterpret_cast<const void*>(kernel);
       flat_cap<kernel>(piece_blocks, kPieceBlocksPerCu<W>, stream, p);
       return hipSuccess;
