@@ -375,6 +375,80 @@ __device__ __forceinline__ void pack_chunk(const float (&acc)[kChunk], u32x4 (&p
   }
 }
 
+// Use every argument the contiguous kernels read (no instruction is
+// emitted), so that their scalar loads issue together at the start of a
+// wave and it waits once for them, instead of once for the bounds and
+// again, after the bounds check, for the base pointers. Measured about 1 %
+// faster on the W=8 H=8192 piece kernel, whose waves are short-lived, and
+// about 0.35 % on the W=8 H=5120 chunk kernel. One asm statement per group:
+// separate statements let the scheduler put a wait between them.
+template <int W>
+__device__ __forceinline__ void pin_flat_args(const KernelArgs& a, uint64_t n, uint32_t m);
+template <>
+__device__ __forceinline__ void pin_flat_args<8>(const KernelArgs& a, uint64_t n, uint32_t m) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.x[2]), "s"(a.x[3]), "s"(a.x[4]), "s"(a.x[5]), "s"(a.x[6]),
+               "s"(a.x[7]));
+  asm volatile("" ::"s"(a.scales[0]), "s"(a.scales[1]), "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.scales[4]),
+               "s"(a.scales[5]), "s"(a.scales[6]), "s"(a.scales[7]), "s"(a.out[0]), "s"(n), "s"(m));
+}
+template <>
+__device__ __forceinline__ void pin_flat_args<4>(const KernelArgs& a, uint64_t n, uint32_t m) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.x[2]), "s"(a.x[3]), "s"(a.scales[0]), "s"(a.scales[1]),
+               "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.out[0]), "s"(n), "s"(m));
+}
+template <>
+__device__ __forceinline__ void pin_flat_args<2>(const KernelArgs& a, uint64_t n, uint32_t m) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.scales[0]), "s"(a.scales[1]), "s"(a.out[0]), "s"(n), "s"(m));
+}
+
+// The same for the piece kernel's row-strided form (row split and strides
+// too; -1.7 % on the W=8 H=8192 strided share) and all-shares form (share
+// strides; -0.4 % on the W=8 H=8192 group).
+template <int W>
+__device__ __forceinline__ void pin_rows_args(const KernelArgs& a);
+template <>
+__device__ __forceinline__ void pin_rows_args<8>(const KernelArgs& a) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.x[2]), "s"(a.x[3]), "s"(a.x[4]), "s"(a.x[5]), "s"(a.x[6]),
+               "s"(a.x[7]), "s"(a.out[0]), "s"(a.total_chunks), "s"(a.pair_limit), "s"(a.chunks_per_row),
+               "s"(a.div_magic));
+  asm volatile("" ::"s"(a.scales[0]), "s"(a.scales[1]), "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.scales[4]),
+               "s"(a.scales[5]), "s"(a.scales[6]), "s"(a.scales[7]), "s"(a.x_row_stride), "s"(a.scale_row_stride),
+               "s"(a.out_row_stride));
+}
+template <>
+__device__ __forceinline__ void pin_rows_args<4>(const KernelArgs& a) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.x[2]), "s"(a.x[3]), "s"(a.scales[0]), "s"(a.scales[1]),
+               "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.out[0]), "s"(a.total_chunks), "s"(a.pair_limit),
+               "s"(a.chunks_per_row), "s"(a.div_magic), "s"(a.x_row_stride), "s"(a.scale_row_stride),
+               "s"(a.out_row_stride));
+}
+template <>
+__device__ __forceinline__ void pin_rows_args<2>(const KernelArgs& a) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.scales[0]), "s"(a.scales[1]), "s"(a.out[0]),
+               "s"(a.total_chunks), "s"(a.pair_limit), "s"(a.chunks_per_row), "s"(a.div_magic), "s"(a.x_row_stride),
+               "s"(a.scale_row_stride), "s"(a.out_row_stride));
+}
+template <int W>
+__device__ __forceinline__ void pin_shares_args(const KernelArgs& a);
+template <>
+__device__ __forceinline__ void pin_shares_args<8>(const KernelArgs& a) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.x[2]), "s"(a.x[3]), "s"(a.x[4]), "s"(a.x[5]), "s"(a.x[6]),
+               "s"(a.x[7]), "s"(a.total_chunks), "s"(a.pair_limit), "s"(a.x_share_stride), "s"(a.scale_share_stride));
+  asm volatile("" ::"s"(a.scales[0]), "s"(a.scales[1]), "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.scales[4]),
+               "s"(a.scales[5]), "s"(a.scales[6]), "s"(a.scales[7]));
+}
+template <>
+__device__ __forceinline__ void pin_shares_args<4>(const KernelArgs& a) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.x[2]), "s"(a.x[3]), "s"(a.scales[0]), "s"(a.scales[1]),
+               "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.total_chunks), "s"(a.pair_limit), "s"(a.x_share_stride),
+               "s"(a.scale_share_stride));
+}
+template <>
+__device__ __forceinline__ void pin_shares_args<2>(const KernelArgs& a) {
+  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.scales[0]), "s"(a.scales[1]), "s"(a.total_chunks),
+               "s"(a.pair_limit), "s"(a.x_share_stride), "s"(a.scale_share_stride));
+}
+
 // Addressing of a launch: one contiguous share (no per-block offset
 // arithmetic: the hot path), one share with row-strided slices and output,
 // or all W shares of contiguous pre-all-to-all inputs (blockIdx.y = share).
@@ -398,6 +472,7 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
   constexpr int CH = QRS_CHUNKS_PER_LANE;
   constexpr int P = OutPieces<OF>::kCount;
   static_assert(!ROWS || CH <= 2, "row split assumes a lane's offset from its block's first chunk < 1024");
+  if constexpr (OFF32) pin_flat_args<W>(a, a.chunks_per_row, 0u);
   uint32_t block_id = blockIdx.x;
 #if QRS_XCD_REMAP
   if ((gridDim.x & 7u) == 0) block_id = (block_id & 7u) * (gridDim.x >> 3) + (block_id >> 3);
@@ -620,34 +695,6 @@ __device__ __forceinline__ void fold_piece(const u32x2 (&xv)[W], const float (&s
   }
 }
 
-// Uses every argument the contiguous piece kernel reads (no instruction is
-// emitted), so that their scalar loads issue together at the start of a
-// wave and it waits once for them, instead of once for the bounds and
-// again, after the bounds check, for the base pointers (measured about 1 %
-// faster on the W=8 H=8192 share, whose waves are short-lived). One asm
-// statement per group: separate statements let the scheduler put a wait
-// between them.
-template <int W>
-__device__ __forceinline__ void pin_flat_args(const KernelArgs& a);
-template <>
-__device__ __forceinline__ void pin_flat_args<8>(const KernelArgs& a) {
-  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.x[2]), "s"(a.x[3]), "s"(a.x[4]), "s"(a.x[5]), "s"(a.x[6]),
-               "s"(a.x[7]));
-  asm volatile("" ::"s"(a.scales[0]), "s"(a.scales[1]), "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.scales[4]),
-               "s"(a.scales[5]), "s"(a.scales[6]), "s"(a.scales[7]), "s"(a.out[0]), "s"(a.total_chunks),
-               "s"(a.pair_limit));
-}
-template <>
-__device__ __forceinline__ void pin_flat_args<4>(const KernelArgs& a) {
-  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.x[2]), "s"(a.x[3]), "s"(a.scales[0]), "s"(a.scales[1]),
-               "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.out[0]), "s"(a.total_chunks), "s"(a.pair_limit));
-}
-template <>
-__device__ __forceinline__ void pin_flat_args<2>(const KernelArgs& a) {
-  asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.scales[0]), "s"(a.scales[1]), "s"(a.out[0]),
-               "s"(a.total_chunks), "s"(a.pair_limit));
-}
-
 // Shares with MX scales and a 16-bit output: lane l of block b owns piece
 // p = b * QRS_BLOCK + l of the share, elements [8p, 8p + 8). It loads 8 code
 // bytes per rank (one 8-byte load; a wave's load covers 512 contiguous bytes
@@ -666,7 +713,9 @@ template <int W, int XF, int OF, int ADDR>
 __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
   static_assert(OF != kOutF32 && XF != kXInt8, "MX scales with a 16-bit output");
   static_assert(ADDR == kAddrFlat32 || ADDR == kAddrShares || ADDR == kAddrRows, "addressing");
-  if constexpr (ADDR == kAddrFlat32) pin_flat_args<W>(a);
+  if constexpr (ADDR == kAddrFlat32) pin_flat_args<W>(a, a.total_chunks, a.pair_limit);
+  if constexpr (ADDR == kAddrRows) pin_rows_args<W>(a);
+  if constexpr (ADDR == kAddrShares) pin_shares_args<W>(a);
   const uint64_t n_pieces = a.total_chunks * 2;
   uint32_t b = blockIdx.x;
 #if QRS_PIECE_XCD_PAIRS
