@@ -94,6 +94,16 @@
 #ifndef QRS_MX16_PIECES
 #define QRS_MX16_PIECES 1
 #endif
+// The same for MX scales with an fp32 output, from this world size up
+// (0 = never). Each lane's 32 output bytes go out as two 16-byte stores
+// after a trade across the half-waves, so each store instruction still
+// writes 1 KiB contiguously. Measured at W = 8 against chunks (whole
+// library, one box, 4 rounds, medians, outputs identical): the H = 5120
+// share -2.4 %, the H = 8192 share -3.8 %, row-strided -1.8 and -2.8 %,
+// all shares -0.9 %; at W = 4 a tie, at W = 2 +5.8 %.
+#ifndef QRS_MX32_PIECES_MIN_WORLD
+#define QRS_MX32_PIECES_MIN_WORLD 8
+#endif
 // The chunk kernel's row-strided blocks, renumbered in pairs per XCD like
 // the piece kernel's (1) or in hardware order (0).
 #ifndef QRS_ROWS_XCD_PAIRS
@@ -663,9 +673,33 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_kernel(KernelArgs a) {
 
 // acc[0..7] = rank-ordered fold of the dequantized products of one
 // 8-element piece (decode, then one rounded multiply and one rounded add per
-// rank, as in fold_chunk).
-template <int W, int XF>
+// rank, as in fold_chunk; with SCALED, each product one scaled conversion).
+template <int W, int XF, bool SCALED>
 __device__ __forceinline__ void fold_piece(const u32x2 (&xv)[W], const float (&sv)[W], float (&acc)[8]) {
+  if constexpr (SCALED) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const f32x2 lo = product_pair<XF, true>(xv[0][q], sv[0], false);
+      const f32x2 hi = product_pair<XF, true>(xv[0][q], sv[0], true);
+      acc[4 * q + 0] = lo.x;
+      acc[4 * q + 1] = lo.y;
+      acc[4 * q + 2] = hi.x;
+      acc[4 * q + 3] = hi.y;
+    }
+#pragma unroll
+    for (int r = 1; r < W; ++r) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const f32x2 lo = product_pair<XF, true>(xv[r][q], sv[r], false);
+        const f32x2 hi = product_pair<XF, true>(xv[r][q], sv[r], true);
+        acc[4 * q + 0] = acc[4 * q + 0] + lo.x;
+        acc[4 * q + 1] = acc[4 * q + 1] + lo.y;
+        acc[4 * q + 2] = acc[4 * q + 2] + hi.x;
+        acc[4 * q + 3] = acc[4 * q + 3] + hi.y;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const uint32_t w = xv[0][q];
@@ -695,12 +729,36 @@ __device__ __forceinline__ void fold_piece(const u32x2 (&xv)[W], const float (&s
   }
 }
 
-// Shares with MX scales and a 16-bit output: lane l of block b owns piece
-// p = b * QRS_BLOCK + l of the share, elements [8p, 8p + 8). It loads 8 code
-// bytes per rank (one 8-byte load; a wave's load covers 512 contiguous bytes
-// of a row) and the piece's E8M0 byte (element 8p's block of 32), folds,
-// converts to 8 16-bit values and writes them with one 16-byte store, so a
-// wave's store covers 1 KiB of a row contiguously. Addressing:
+// Writes 16-byte unit u (of 128) of the fp32 output of the wave whose first
+// piece is wave_first: unit u holds elements [4u, 4u + 4) of the wave's
+// 512, half (u & 1) of piece wave_first + u / 2. Nothing past the share.
+template <int ADDR>
+__device__ __forceinline__ void store_piece_unit(const KernelArgs& a, uint64_t wave_first, uint32_t u,
+                                                 uint64_t n_pieces, const u32x4& v) {
+  const uint64_t q = wave_first + (u >> 1);
+  if (q >= n_pieces) return;
+  if constexpr (ADDR == kAddrFlat32) {
+    store_stream(reinterpret_cast<u32x4*>(static_cast<char*>(a.out[0]) +
+                                          (static_cast<uint32_t>(wave_first) * 2u + u) * 16u),
+                 v);
+  } else if constexpr (ADDR == kAddrShares) {
+    store_stream(static_cast<u32x4*>(a.out[blockIdx.y]) + wave_first * 2 + u, v);
+  } else {
+    const uint64_t ppr = a.chunks_per_row * 2;
+    const uint64_t row = __umul64hi(q, a.div_magic);
+    const uint64_t col = q - row * ppr;
+    store_stream(static_cast<u32x4*>(a.out[0]) + row * a.out_row_stride + col * 2 + (u & 1u), v);
+  }
+}
+
+// Shares with MX scales: lane l of block b owns piece p = b * QRS_BLOCK + l
+// of the share, elements [8p, 8p + 8). It loads 8 code bytes per rank (one
+// 8-byte load; a wave's load covers 512 contiguous bytes of a row) and the
+// piece's E8M0 byte (element 8p's block of 32), and folds. A 16-bit output
+// is converted and written with one 16-byte store, so a wave's store covers
+// 1 KiB of a row contiguously. An fp32 output is two 16-byte units per lane;
+// the two halves of the wave trade units first, so that each of the wave's
+// two stores covers 1 KiB contiguously as well. Addressing:
 //   kAddrFlat32  one contiguous share, every slice, scale slice and the
 //                output under 4 GiB (32-bit offsets on the scalar bases);
 //   kAddrShares  all W shares of contiguous pre-all-to-all inputs: share
@@ -711,7 +769,9 @@ __device__ __forceinline__ void fold_piece(const u32x2 (&xv)[W], const float (&s
 //                multiply by div_magic = ceil(2^64 / (H / 8)).
 template <int W, int XF, int OF, int ADDR>
 __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
-  static_assert(OF != kOutF32 && XF != kXInt8, "MX scales with a 16-bit output");
+  static_assert(XF != kXInt8, "MX scales with fp8 codes");
+  constexpr bool F32 = OF == kOutF32;
+  constexpr bool SCALED = kScaledCvt<kScaleE8M0Block32, OF>;
   static_assert(ADDR == kAddrFlat32 || ADDR == kAddrShares || ADDR == kAddrRows, "addressing");
   if constexpr (ADDR == kAddrFlat32) pin_flat_args<W>(a, a.total_chunks, a.pair_limit);
   if constexpr (ADDR == kAddrRows) pin_rows_args<W>(a);
@@ -727,11 +787,20 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
   // line is fetched into one L2.
   if (b < a.pair_limit) b = (b & ~15u) | ((b & 7u) << 1) | ((b >> 3) & 1u);
 #endif
-  const uint64_t p = static_cast<uint64_t>(b) * QRS_BLOCK + threadIdx.x;
-  if (p >= n_pieces) return;
+  uint64_t p = static_cast<uint64_t>(b) * QRS_BLOCK + threadIdx.x;
+  [[maybe_unused]] uint64_t wave_first = 0;
+  if constexpr (F32) {
+    // The trade of output units needs the whole wave: lanes past the end
+    // load the last piece again and store nothing.
+    wave_first = static_cast<uint64_t>(b) * QRS_BLOCK + (threadIdx.x & ~63u);
+    if (wave_first >= n_pieces) return;
+    p = p < n_pieces ? p : n_pieces - 1;
+  } else {
+    if (p >= n_pieces) return;
+  }
   u32x2 xv[W];
   float sv[W];
-  u32x4* dst;
+  [[maybe_unused]] u32x4* dst = nullptr;
   if constexpr (ADDR == kAddrFlat32) {
     // 32-bit offsets on the scalar bases for the codes and the scale bytes.
     const uint32_t p32 = static_cast<uint32_t>(p);
@@ -741,8 +810,8 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
     for (int r = 0; r < W; ++r)
       xv[r] = load_stream(reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(a.x[r]) + xb));
 #pragma unroll
-    for (int r = 0; r < W; ++r) sv[r] = decode_e8m0(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
-    dst = reinterpret_cast<u32x4*>(static_cast<char*>(a.out[0]) + p32 * 16u);
+    for (int r = 0; r < W; ++r) sv[r] = mx_scale_operand<SCALED>(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
+    if constexpr (!F32) dst = reinterpret_cast<u32x4*>(static_cast<char*>(a.out[0]) + p32 * 16u);
   } else if constexpr (ADDR == kAddrShares) {
     const uint32_t share = blockIdx.y;
     const uint64_t xb = share * a.x_share_stride * sizeof(u32x4) + p * 8u;
@@ -751,8 +820,8 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
     for (int r = 0; r < W; ++r)
       xv[r] = load_stream(reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(a.x[r]) + xb));
 #pragma unroll
-    for (int r = 0; r < W; ++r) sv[r] = decode_e8m0(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
-    dst = static_cast<u32x4*>(a.out[share]) + p;
+    for (int r = 0; r < W; ++r) sv[r] = mx_scale_operand<SCALED>(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
+    if constexpr (!F32) dst = static_cast<u32x4*>(a.out[share]) + p;
   } else {
     const uint64_t ppr = a.chunks_per_row * 2;  // pieces per row
     const uint64_t row = __umul64hi(p, a.div_magic);
@@ -764,11 +833,30 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
     for (int r = 0; r < W; ++r)
       xv[r] = load_stream(reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(a.x[r]) + xb));
 #pragma unroll
-    for (int r = 0; r < W; ++r) sv[r] = decode_e8m0(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
-    dst = static_cast<u32x4*>(a.out[0]) + row * a.out_row_stride + col;
+    for (int r = 0; r < W; ++r) sv[r] = mx_scale_operand<SCALED>(*(static_cast<const uint8_t*>(a.scales[r]) + sb));
+    if constexpr (!F32) dst = static_cast<u32x4*>(a.out[0]) + row * a.out_row_stride + col;
   }
   float acc[8];
-  fold_piece<W, XF>(xv, sv, acc);
+  fold_piece<W, XF, SCALED>(xv, sv, acc);
+  if constexpr (F32) {
+    // Lane l holds units 2l and 2l + 1 of the wave's 128 (16 bytes each).
+    // Trading the lower half-wave's second units for the upper half-wave's
+    // first leaves lane l < 32 with units 2l and 2l + 64 and lane l >= 32
+    // with units 2l - 63 and 2l + 1: the first store writes units 0..63,
+    // the second 64..127.
+    u32x4 lo, hi;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, acc[d]),
+                                                      __builtin_bit_cast(uint32_t, acc[4 + d]), false, false);
+      lo[d] = r[0];
+      hi[d] = r[1];
+    }
+    const uint32_t lane = threadIdx.x & 63u;
+    store_piece_unit<ADDR>(a, wave_first, lane < 32u ? 2u * lane : 2u * lane - 63u, n_pieces, lo);
+    store_piece_unit<ADDR>(a, wave_first, lane < 32u ? 2u * lane + 64u : 2u * lane + 1u, n_pieces, hi);
+    return;
+  }
   uint32_t packed[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -784,10 +872,13 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
 }
 
 // Whether a kernel instantiation takes the piece layout.
-template <int SL, int OF>
-constexpr bool kPieceLayout = QRS_MX16_PIECES && SL == kScaleE8M0Block32 && OF != kOutF32;
+template <int W, int SL, int OF>
+constexpr bool kPieceLayout =
+    SL == kScaleE8M0Block32 &&
+    (OF == kOutF32 ? (QRS_MX32_PIECES_MIN_WORLD > 0 && W >= QRS_MX32_PIECES_MIN_WORLD) : QRS_MX16_PIECES);
 
-// Blocks resident per CU for the piece kernel (0 = no cap), by world size.
+// Blocks resident per CU for the piece kernel with a 16-bit output (0 = no
+// cap), by world size.
 // A lane keeps W 8-byte loads in flight: at W = 8 six blocks per CU
 // measured best (W=8 shares with H = 8192 and 5120; 4 and 5 slower), at
 // W = 2 and 4 full occupancy (capped at 4 or 6 blocks they ran 0-16 %
@@ -801,9 +892,23 @@ constexpr bool kPieceLayout = QRS_MX16_PIECES && SL == kScaleE8M0Block32 && OF !
 #ifndef QRS_PIECE_BLOCKS_PER_CU_W2
 #define QRS_PIECE_BLOCKS_PER_CU_W2 0
 #endif
-template <int W>
+// With an fp32 output a lane also keeps 32 output bytes, and at W = 8 four
+// blocks per CU measured best (5 the same within noise; 6 +1.5 %, 8 and
+// no cap +3.3 % on the H = 5120 share).
+#ifndef QRS_PIECE32_BLOCKS_PER_CU_W8
+#define QRS_PIECE32_BLOCKS_PER_CU_W8 4
+#endif
+#ifndef QRS_PIECE32_BLOCKS_PER_CU_W4
+#define QRS_PIECE32_BLOCKS_PER_CU_W4 0
+#endif
+#ifndef QRS_PIECE32_BLOCKS_PER_CU_W2
+#define QRS_PIECE32_BLOCKS_PER_CU_W2 0
+#endif
+template <int W, int OF>
 constexpr uint32_t kPieceBlocksPerCu =
-    W >= 8 ? QRS_PIECE_BLOCKS_PER_CU_W8 : (W >= 4 ? QRS_PIECE_BLOCKS_PER_CU_W4 : QRS_PIECE_BLOCKS_PER_CU_W2);
+    OF == kOutF32
+        ? (W >= 8 ? QRS_PIECE32_BLOCKS_PER_CU_W8 : (W >= 4 ? QRS_PIECE32_BLOCKS_PER_CU_W4 : QRS_PIECE32_BLOCKS_PER_CU_W2))
+        : (W >= 8 ? QRS_PIECE_BLOCKS_PER_CU_W8 : (W >= 4 ? QRS_PIECE_BLOCKS_PER_CU_W4 : QRS_PIECE_BLOCKS_PER_CU_W2));
 
 // One launch, chosen but not yet enqueued: the kernel instantiation, its
 // grid, the dynamic LDS that caps residency, and the launch device's sizes
@@ -897,7 +1002,7 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
   const uint64_t piece_blocks = (a.total_chunks * 2 + QRS_BLOCK - 1) / QRS_BLOCK;
   if (l.n_shares > 1) {
     if (l.n_rows != 1) return hipErrorInvalidValue;
-    if constexpr (kPieceLayout<SL, OF>) {
+    if constexpr (kPieceLayout<W, SL, OF>) {
       if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
       p->grid = dim3(static_cast<uint32_t>(piece_blocks), l.n_shares);
       a.pair_limit = static_cast<uint32_t>(piece_blocks) & ~15u;
@@ -908,7 +1013,7 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
     return hipSuccess;
   }
   if (l.n_rows > 1) {
-    if constexpr (kPieceLayout<SL, OF>) {
+    if constexpr (kPieceLayout<W, SL, OF>) {
       if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
       a.div_magic = ~0ull / (a.chunks_per_row * 2) + 1;  // rows of H / 8 pieces
       p->grid = dim3(static_cast<uint32_t>(piece_blocks));
@@ -922,13 +1027,13 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
   // The output is the largest of the share's tensors (at least 2 bytes per
   // element against 1 + 1/32 for a slice and its scales).
   if (a.chunks_per_row * OutPieces<OF>::kCount * sizeof(u32x4) < (1ull << 32)) {
-    if constexpr (kPieceLayout<SL, OF>) {
+    if constexpr (kPieceLayout<W, SL, OF>) {
       if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
       constexpr auto kernel = reduce_piece_kernel<W, XF, OF, kAddrFlat32>;
       p->grid = dim3(static_cast<uint32_t>(piece_blocks));
       a.pair_limit = static_cast<uint32_t>(piece_blocks) & ~15u;
       p->kernel = reinterpret_cast<const void*>(kernel);
-      flat_cap<kernel>(piece_blocks, kPieceBlocksPerCu<W>, stream, p);
+      flat_cap<kernel>(piece_blocks, kPieceBlocksPerCu<W, OF>, stream, p);
       return hipSuccess;
     }
     constexpr auto kernel = reduce_kernel<W, XF, SL, OF, kAddrFlat32>;

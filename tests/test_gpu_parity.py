@@ -350,13 +350,17 @@ def test_share_writes_only_its_output(gpu, x_format, scale_layout, out_dtype, w,
     (4, 37, 1152),   # 21 blocks, the last one partial
     (2, 64, 8192),   # 256 blocks, every one paired
     (8, 31, 5120),   # 78 blocks, the last one partial
+    (8, 37, 1152),   # 21 blocks, the last wave partial; waves straddle rows
 ])
-@pytest.mark.parametrize("out_dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("out_dtype", ["bf16", "f16", "f32"])
 def test_piece_grids_with_unpaired_tails(gpu, w, rows, h, out_dtype):
-    """MX shares with 16-bit outputs run as 8-element pieces with blocks
-    renumbered in groups of 16: grids whose block count is not a multiple of
-    16 (and whose last block is partial) must still cover every element once,
-    through all three launch forms."""
+    """MX shares run as 8-element pieces (fp32 outputs from W = 8) with
+    blocks renumbered in groups of 16: grids whose block count is not a
+    multiple of 16 (and whose last block or wave is partial) must still
+    cover every element once, through all three launch forms. fp32 pieces
+    trade output units across the half-waves, so a wave past the end of the
+    share or straddling two rows must still store each unit at its own
+    place."""
     import quantized_collective_reduction_amd as qrs
 
     wl = workloads.Workload("tails", w, rows * w, h, "e4m3fn", "e8m0_block32", out_dtype, x_dist="normal",
