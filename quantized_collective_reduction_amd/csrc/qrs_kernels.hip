@@ -97,12 +97,13 @@
 // The same for MX scales with an fp32 output, from this world size up
 // (0 = never). Each lane's 32 output bytes go out as two 16-byte stores
 // after a trade across the half-waves, so each store instruction still
-// writes 1 KiB contiguously. Measured at W = 8 against chunks (whole
-// library, one box, 4 rounds, medians, outputs identical): the H = 5120
-// share -2.4 %, the H = 8192 share -3.8 %, row-strided -1.8 and -2.8 %,
-// all shares -0.9 %; at W = 4 a tie, at W = 2 +5.8 %.
+// writes 1 KiB contiguously. Measured against chunks (whole library, one
+// box, 4 rounds, medians, outputs identical): at W = 8 the H = 5120 share
+// -2.4 %, the H = 8192 share -3.8 %, row-strided -1.8 and -2.8 %, all
+// shares -0.9 %; at W = 4 (6 blocks per CU) -1.7 and -0.6 %; at W = 2
+// +1.7 % at best (6 blocks per CU).
 #ifndef QRS_MX32_PIECES_MIN_WORLD
-#define QRS_MX32_PIECES_MIN_WORLD 8
+#define QRS_MX32_PIECES_MIN_WORLD 4
 #endif
 // The chunk kernel's row-strided blocks, renumbered in pairs per XCD like
 // the piece kernel's (1) or in hardware order (0).
@@ -877,6 +878,24 @@ constexpr bool kPieceLayout =
     SL == kScaleE8M0Block32 &&
     (OF == kOutF32 ? (QRS_MX32_PIECES_MIN_WORLD > 0 && W >= QRS_MX32_PIECES_MIN_WORLD) : QRS_MX16_PIECES);
 
+// Blocks resident per CU for the all-shares piece launch (0 = no cap), by
+// world size. At W = 8 four (one box, 4 rounds, medians, against no cap:
+// the H = 8192 MX group -1.3 % with bf16 out and -3.0 % with fp32 out; 5
+// the same, 6 -0.1 / -2.2 %, 8 no change); at W = 4 none (4 to 6 blocks
+// +4 to +16 %).
+#ifndef QRS_PIECE_SHARES_BLOCKS_PER_CU_W8
+#define QRS_PIECE_SHARES_BLOCKS_PER_CU_W8 4
+#endif
+#ifndef QRS_PIECE_SHARES_BLOCKS_PER_CU_W4
+#define QRS_PIECE_SHARES_BLOCKS_PER_CU_W4 0
+#endif
+#ifndef QRS_PIECE_SHARES_BLOCKS_PER_CU_W2
+#define QRS_PIECE_SHARES_BLOCKS_PER_CU_W2 0
+#endif
+template <int W>
+constexpr uint32_t kPieceSharesBlocksPerCu =
+    W >= 8 ? QRS_PIECE_SHARES_BLOCKS_PER_CU_W8
+           : (W >= 4 ? QRS_PIECE_SHARES_BLOCKS_PER_CU_W4 : QRS_PIECE_SHARES_BLOCKS_PER_CU_W2);
 // Blocks resident per CU for the piece kernel with a 16-bit output (0 = no
 // cap), by world size.
 // A lane keeps W 8-byte loads in flight: at W = 8 six blocks per CU
@@ -894,12 +913,13 @@ constexpr bool kPieceLayout =
 #endif
 // With an fp32 output a lane also keeps 32 output bytes, and at W = 8 four
 // blocks per CU measured best (5 the same within noise; 6 +1.5 %, 8 and
-// no cap +3.3 % on the H = 5120 share).
+// no cap +3.3 % on the H = 5120 share); at W = 4 six (4 and 8 slower
+// than chunks).
 #ifndef QRS_PIECE32_BLOCKS_PER_CU_W8
 #define QRS_PIECE32_BLOCKS_PER_CU_W8 4
 #endif
 #ifndef QRS_PIECE32_BLOCKS_PER_CU_W4
-#define QRS_PIECE32_BLOCKS_PER_CU_W4 0
+#define QRS_PIECE32_BLOCKS_PER_CU_W4 6
 #endif
 #ifndef QRS_PIECE32_BLOCKS_PER_CU_W2
 #define QRS_PIECE32_BLOCKS_PER_CU_W2 0
@@ -1006,7 +1026,9 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
       if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
       p->grid = dim3(static_cast<uint32_t>(piece_blocks), l.n_shares);
       a.pair_limit = static_cast<uint32_t>(piece_blocks) & ~15u;
-      p->kernel = reinterpret_cast<const void*>(reduce_piece_kernel<W, XF, OF, kAddrShares>);
+      constexpr auto kernel = reduce_piece_kernel<W, XF, OF, kAddrShares>;
+      p->kernel = reinterpret_cast<const void*>(kernel);
+      flat_cap<kernel>(piece_blocks * l.n_shares, kPieceSharesBlocksPerCu<W>, stream, p);
       return hipSuccess;
     }
     p->kernel = reinterpret_cast<const void*>(reduce_kernel<W, XF, SL, OF, kAddrShares>);

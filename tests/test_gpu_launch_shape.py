@@ -18,7 +18,7 @@ ATTR_MAX_SHARED_MEMORY_PER_MULTIPROCESSOR = 10002
 ATTR_MAX_SHARED_MEMORY_PER_BLOCK = 74
 BLOCKS_PER_CU = 4  # the library's cap for large contiguous shares of 16-element chunks
 PIECE_BLOCKS_PER_CU_W8 = 6  # ... and of 8-element pieces (MX scales, 16-bit output) at W = 8
-PIECE32_BLOCKS_PER_CU_W8 = 4  # ... and of fp32-output pieces at W = 8
+PIECE32_BLOCKS_PER_CU = {8: 4, 4: 6}  # ... and of fp32-output pieces (W = 8 and 4)
 
 
 def _hip_attr(attr, dev=0):
@@ -54,10 +54,10 @@ def test_device_sizes_are_the_runtimes(gpu):
 def _expected_layout(w, sl, od):
     """Elements per lane and blocks per CU of the contiguous share: MX scales
     with a 16-bit output take 8-element pieces, capped at 6 blocks per CU at
-    W = 8 and uncapped below; with an fp32 output pieces at W = 8, capped at
-    4; every other mode 16-element chunks capped at 4."""
-    if sl == "e8m0_block32" and od == "f32" and w == 8:
-        return 8, PIECE32_BLOCKS_PER_CU_W8
+    W = 8 and uncapped below; with an fp32 output pieces at W = 8 and 4,
+    capped at 4 and 6; every other mode 16-element chunks capped at 4."""
+    if sl == "e8m0_block32" and od == "f32" and w in PIECE32_BLOCKS_PER_CU:
+        return 8, PIECE32_BLOCKS_PER_CU[w]
     if sl == "e8m0_block32" and od != "f32":
         return 8, (PIECE_BLOCKS_PER_CU_W8 if w == 8 else 0)
     return 16, BLOCKS_PER_CU
@@ -68,7 +68,8 @@ def _expected_layout(w, sl, od):
     (8, 16384, 8192, "e5m2", "e8m0_block32", "f16"),      # 8192 piece blocks
     (4, 8192, 8192, "e4m3fn", "e8m0_block32", "bf16"),    # 8192 piece blocks, uncapped at W = 4
     (8, 65536, 5120, "e5m2", "e8m0_block32", "f32"),      # 20480 piece blocks
-    (4, 32768, 8192, "e5m2", "e8m0_block32", "f32"),      # 16384 blocks: chunks at W = 4, fp32 staging in LDS
+    (4, 32768, 8192, "e5m2", "e8m0_block32", "f32"),      # 32768 piece blocks, capped at 6
+    (2, 16384, 8192, "e4m3fn", "e8m0_block32", "f32"),    # 16384 blocks: chunks at W = 2, fp32 staging in LDS
     (2, 8192, 8192, "int8", "f32_group128", "f32"),       # 8192 blocks
     (8, 16384, 8192, "e4m3fn", "f32_group128", "bf16"),   # 4096 blocks
 ])
