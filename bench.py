@@ -2,7 +2,8 @@
 reduce-scatter (dequant + rank-ordered reduce) on MI355X.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--op OP] [--layout L]
-                    [--hot] [--overlap] [--no-cpu-baseline] [--no-largest] [--gpus 1]
+                    [--hot] [--overlap] [--size-sweep] [--no-cpu-baseline] [--no-largest]
+                    [--gpus 1]
 
 A step is one launch of the whole hot path (decode, scale, rank-ordered fp32
 fold, convert, store) over one batch: W rank slices of the workload, already
@@ -42,6 +43,12 @@ Prints ONE JSON line on stdout:
                    over two streams of the default priority (independent
                    batches, each stream on its own rotating sets), wall
                    time per step; else null.
+  size_sweep       with --size-sweep (--op share), context only: the share
+                   kernel and the stream copy timed at 1024 to 8192 rows per
+                   slice of the workload's W, H and types (events over
+                   back-to-back rotating launches, like the steps), and the
+                   least-squares fit time = fixed + bytes / rate of each;
+                   else null.
   largest_workload with --op share (the default), unless --no-largest: the
                    largest workload (W=8, BS=65536, H=5120, MX E5M2 -> fp32)
                    timed the same way in the same run, after the headline
@@ -389,6 +396,80 @@ def time_largest(args, dev, qrs, workloads, torch):
     }
 
 
+# Rows per slice of the size sweep. Below about 1024 rows a launch at W = 8
+# takes less device time than the host needs to enqueue it (about 5-8 us
+# through the binding), so smaller points would measure the host.
+SWEEP_ROWS = (1024, 1536, 2048, 3072, 4096, 6144, 8192)
+
+
+def time_copy(nbytes, n_sets, warmup, steps, dev, qrs, torch, stream):
+    """The plain 16-byte stream copy moving nbytes (half read, half
+    written), rotating over n_sets buffer pairs, timed like the steps.
+    Returns seconds per copy."""
+    half = (nbytes // 2) // 16 * 16
+    src = torch.empty(half * n_sets, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    pairs = [(src[k * half:(k + 1) * half], dst[k * half:(k + 1) * half]) for k in range(n_sets)]
+    launches = [lambda a=a, b=b: qrs.stream_copy(a, b, stream=stream) for a, b in pairs]
+    _, per = time_steps(launches, warmup, steps, stream, torch)
+    del src, dst, pairs, launches
+    return per
+
+
+def fit_fixed_and_rate(points):
+    """Least-squares line time = fixed + bytes / rate over (bytes, seconds)
+    points: returns (fixed microseconds, rate in GB/s)."""
+    b = np.array([p[0] for p in points], dtype=np.float64)
+    t = np.array([p[1] for p in points], dtype=np.float64)
+    slope, intercept = np.polyfit(b, t, 1)
+    return intercept * 1e6, 1.0 / slope / 1e9
+
+
+def size_sweep(wl, args, dev, qrs, workloads, torch, sweep_rows=SWEEP_ROWS):
+    """The share kernel and the stream copy at sweep_rows rows per slice
+    (ascending) of the workload's shape (W, H, types), inputs sliced from one
+    generated set of the largest size and placed at the recommended pitch."""
+    stream = torch.cuda.current_stream(dev)
+    big = wl.with_(bs=sweep_rows[-1] * wl.world_size)
+    xs_big, ss_big = workloads.generate(big)
+    out_dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[wl.out_dtype]
+    steps = max(50, min(args.steps, 1000))
+    points, kernel_pts, copy_pts = [], [], []
+    for rows in sweep_rows:
+        sub = wl.with_(bs=rows * wl.world_size)
+        alg = sub.algorithmic_bytes()
+        xs = [np.ascontiguousarray(x[:rows]) for x in xs_big]
+        ss = [np.ascontiguousarray(x[:rows]) for x in ss_big]
+        n_sets = max(2, -(-4 * MALL_BYTES // alg))
+        p = qrs.plan(sub.world_size, sub.bs, sub.h, sub.x_format, sub.scale_layout, sub.out_dtype)
+        launches = []
+        for _ in range(n_sets):
+            dx, ds = place_inputs(p, xs, ss, dev, qrs, torch, args.layout)
+            out = torch.empty((rows, sub.h), dtype=out_dt, device=dev)
+            launches.append(qrs.Launch(p, dx, ds, out, stream=stream))
+        _, k_s = time_steps(launches, 20, steps, stream, torch)
+        del launches
+        torch.cuda.empty_cache()
+        c_s = time_copy(alg, n_sets, 20, steps, dev, qrs, torch, stream)
+        torch.cuda.empty_cache()
+        points.append({"rows_per_slice": rows, "bytes": alg, "kernel_us": round(k_s * 1e6, 3),
+                       "copy_us": round(c_s * 1e6, 3)})
+        kernel_pts.append((alg, k_s))
+        copy_pts.append((alg, c_s))
+        log(f"[bench] size sweep: {rows} rows per slice, {alg} bytes: kernel {k_s * 1e6:.2f} us, "
+            f"copy {c_s * 1e6:.2f} us")
+    kf, kr = fit_fixed_and_rate(kernel_pts)
+    cf, cr = fit_fixed_and_rate(copy_pts)
+    return {
+        "shape": f"W={wl.world_size} H={wl.h} x={wl.x_format} scales={wl.scale_layout} out={wl.out_dtype}",
+        "steps_per_point": steps,
+        "points": points,
+        "fit": {"kernel": {"fixed_us": round(kf, 3), "GBps": round(kr, 1)},
+                "copy": {"fixed_us": round(cf, 3), "GBps": round(cr, 1)}},
+        "note": "context only: least-squares time = fixed + bytes / rate over the points",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -410,6 +491,9 @@ def main():
                     help="also time K launches on one input/output set, without rotation (context only)")
     ap.add_argument("--overlap", action="store_true",
                     help="also time K independent steps alternated over two streams (context only)")
+    ap.add_argument("--size-sweep", action="store_true",
+                    help="also time the share kernel and the stream copy at 1024 to 8192 rows per slice and fit "
+                         "time = fixed + bytes / rate (context only; --op share)")
     ap.add_argument("--no-largest", action="store_true",
                     help="skip the largest workload's extra timing (largest_workload = null)")
     args = ap.parse_args()
@@ -520,10 +604,14 @@ def main():
     del src, dst, copies
 
     largest = None
-    if args.op == "share" and not args.no_largest and wl.name != LARGEST:
+    sweep = None
+    if args.op == "share" and (args.size_sweep or (not args.no_largest and wl.name != LARGEST)):
         del launches, outs
         torch.cuda.empty_cache()
-        largest = time_largest(args, dev, qrs, workloads, torch)
+        if not args.no_largest and wl.name != LARGEST:
+            largest = time_largest(args, dev, qrs, workloads, torch)
+        if args.size_sweep:
+            sweep = size_sweep(wl, args, dev, qrs, workloads, torch)
 
     achieved = alg_bytes / avg_launch_s / 1e9
     value = alg_bytes * args.steps / wall / 1e9
@@ -578,6 +666,7 @@ def main():
                              "GBps": round(copy_gbps, 1)},
         "overlap_2streams": overlap,
         "largest_workload": largest,
+        "size_sweep": sweep,
         "hot": None if hot_s is None else {
             "kernel_us_avg": round(hot_s * 1e6, 3), "GBps": round(alg_bytes / hot_s / 1e9, 2),
             "note": "context only: one input/output set, no rotation"},

@@ -138,3 +138,34 @@ def test_overlap_context(gpu, op):
     assert o["us_per_step"] > 0 and o["sets_per_stream"] >= 1
     assert abs(o["GBps"] - d["config"]["algorithmic_bytes_per_step"] / o["us_per_step"] / 1e3) < 0.01 * o["GBps"]
     assert d["value"] > 0 and d["roofline"]["kernel_us_avg"] > 0
+
+
+def test_fit_fixed_and_rate_recovers_a_line():
+    """The size sweep's fit: points on time = 2.5 us + bytes / 6.5 TB/s give
+    back both numbers."""
+    pts = [(b, 2.5e-6 + b / 6.5e12) for b in (1.0e7, 4.3e7, 1.7e8, 6.9e8)]
+    fixed_us, gbps = bench.fit_fixed_and_rate(pts)
+    assert abs(fixed_us - 2.5) < 1e-6 and abs(gbps - 6500.0) < 1e-6
+
+
+@pytest.mark.gpu
+def test_size_sweep_context(gpu):
+    """--size-sweep's points: the share kernel and the stream copy timed at
+    each size, times growing with the bytes, and the fit over them."""
+    import argparse
+
+    import torch
+
+    import quantized_collective_reduction_amd as qrs
+
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS["w8_bs16384_h8192_mx_e4m3_bf16"]
+    args = argparse.Namespace(steps=50, layout="pitched")
+    rows = (1024, 2048, 4096)  # device-bound sizes: each launch outlasts its enqueue
+    d = bench.size_sweep(wl, args, dev, qrs, workloads, torch, sweep_rows=rows)
+    assert [p["rows_per_slice"] for p in d["points"]] == list(rows)
+    assert [p["bytes"] for p in d["points"]] == [wl.with_(bs=r * 8).algorithmic_bytes() for r in rows]
+    for a, b in zip(d["points"], d["points"][1:]):
+        assert b["kernel_us"] > a["kernel_us"] and b["copy_us"] > a["copy_us"]
+    for k in ("kernel", "copy"):
+        assert d["fit"][k]["GBps"] > 0 and d["fit"][k]["fixed_us"] > 0
