@@ -110,6 +110,13 @@
 #ifndef QRS_ROWS_XCD_PAIRS
 #define QRS_ROWS_XCD_PAIRS 0
 #endif
+// The piece kernel's row-strided form when scale rows do not start on
+// 128-byte lines: 1 = each XCD takes runs of consecutive blocks that cover
+// whole rows (so every row's scale lines are fetched into one L2); 0 = the
+// pairs below.
+#ifndef QRS_ROWS_XCD_GROUPS
+#define QRS_ROWS_XCD_GROUPS 1
+#endif
 // The piece kernel's blocks, renumbered so that the two that share each
 // line of scales run on one XCD (see reduce_piece_kernel). 1: on; 0: off.
 #ifndef QRS_PIECE_XCD_PAIRS
@@ -274,10 +281,15 @@ struct KernelArgs {
   uint32_t out_row_stride;    // in 16-byte units
   uint64_t x_share_stride;      // in 16-byte units
   uint64_t scale_share_stride;  // in bytes
-  // Piece kernels: block ids below this (the grid's full groups of 16) are
-  // renumbered in XCD pairs. Read from the arguments, with the rest of
-  // them, rather than from the dispatch packet.
+  // Piece kernels: block ids below this (the grid's full groups of 16, or
+  // of 8 * xcd_group) are renumbered in XCD pairs (or runs). Read from the
+  // arguments, with the rest of them, rather than from the dispatch packet.
   uint32_t pair_limit;
+  // Row-strided piece kernel: when nonzero, each XCD takes runs of
+  // xcd_group consecutive blocks instead of pairs; xcd_group_magic =
+  // ceil(2^32 / xcd_group) divides by it.
+  uint32_t xcd_group;
+  uint32_t xcd_group_magic;
 };
 
 // Orders a wave's LDS writes before its following LDS reads of other lanes'
@@ -424,20 +436,20 @@ __device__ __forceinline__ void pin_rows_args<8>(const KernelArgs& a) {
                "s"(a.div_magic));
   asm volatile("" ::"s"(a.scales[0]), "s"(a.scales[1]), "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.scales[4]),
                "s"(a.scales[5]), "s"(a.scales[6]), "s"(a.scales[7]), "s"(a.x_row_stride), "s"(a.scale_row_stride),
-               "s"(a.out_row_stride));
+               "s"(a.out_row_stride), "s"(a.xcd_group), "s"(a.xcd_group_magic));
 }
 template <>
 __device__ __forceinline__ void pin_rows_args<4>(const KernelArgs& a) {
   asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.x[2]), "s"(a.x[3]), "s"(a.scales[0]), "s"(a.scales[1]),
                "s"(a.scales[2]), "s"(a.scales[3]), "s"(a.out[0]), "s"(a.total_chunks), "s"(a.pair_limit),
                "s"(a.chunks_per_row), "s"(a.div_magic), "s"(a.x_row_stride), "s"(a.scale_row_stride),
-               "s"(a.out_row_stride));
+               "s"(a.out_row_stride), "s"(a.xcd_group), "s"(a.xcd_group_magic));
 }
 template <>
 __device__ __forceinline__ void pin_rows_args<2>(const KernelArgs& a) {
   asm volatile("" ::"s"(a.x[0]), "s"(a.x[1]), "s"(a.scales[0]), "s"(a.scales[1]), "s"(a.out[0]),
                "s"(a.total_chunks), "s"(a.pair_limit), "s"(a.chunks_per_row), "s"(a.div_magic), "s"(a.x_row_stride),
-               "s"(a.scale_row_stride), "s"(a.out_row_stride));
+               "s"(a.scale_row_stride), "s"(a.out_row_stride), "s"(a.xcd_group), "s"(a.xcd_group_magic));
 }
 template <int W>
 __device__ __forceinline__ void pin_shares_args(const KernelArgs& a);
@@ -786,7 +798,23 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
   // XCD: within each full group of 16 ids (below pair_limit), id
   // 16g + 8h + x takes the pieces of block 16g + 2x + h, and each scale
   // line is fetched into one L2.
-  if (b < a.pair_limit) b = (b & ~15u) | ((b & 7u) << 1) | ((b >> 3) & 1u);
+  if constexpr (ADDR == kAddrRows) {
+    if (b < a.pair_limit) {
+      if (a.xcd_group != 0) {
+        // Runs: XCD x's k-th block (b = 8k + x) takes block
+        // ((k div G) * 8 + x) * G + k mod G, G = xcd_group, so each XCD
+        // walks G consecutive blocks at a time; G * 256 pieces cover whole
+        // rows, so no scale row is split between two XCDs' runs.
+        const uint32_t k = b >> 3;
+        const uint32_t q = __umulhi(k, a.xcd_group_magic);
+        b = ((q << 3) + (b & 7u)) * a.xcd_group + (k - q * a.xcd_group);
+      } else {
+        b = (b & ~15u) | ((b & 7u) << 1) | ((b >> 3) & 1u);
+      }
+    }
+  } else if (b < a.pair_limit) {
+    b = (b & ~15u) | ((b & 7u) << 1) | ((b >> 3) & 1u);
+  }
 #endif
   uint64_t p = static_cast<uint64_t>(b) * QRS_BLOCK + threadIdx.x;
   [[maybe_unused]] uint64_t wave_first = 0;
@@ -1040,6 +1068,28 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
       a.div_magic = ~0ull / (a.chunks_per_row * 2) + 1;  // rows of H / 8 pieces
       p->grid = dim3(static_cast<uint32_t>(piece_blocks));
       a.pair_limit = static_cast<uint32_t>(piece_blocks) & ~15u;
+#if QRS_ROWS_XCD_GROUPS
+      // Scale rows off 128-byte lines (a row's bytes, its stride or a rank's
+      // base): lines are shared between ranks' rows and between rows, so
+      // give each XCD runs of blocks covering whole rows (G = lcm(pieces per
+      // row, 256) / 256 <= 64), unless the grid holds no full set of runs.
+      bool misaligned = (l.row_elems / 32) % 128 != 0 || l.scale_row_stride % 128 != 0;
+      for (int r = 0; r < W; ++r) misaligned |= reinterpret_cast<uintptr_t>(l.scales[r]) % 128 != 0;
+      const uint64_t ppr = a.chunks_per_row * 2;
+      uint64_t g = 256;
+      for (uint64_t m = ppr; m != 0;) {  // g = gcd(ppr, 256)
+        const uint64_t t = g % m;
+        g = m;
+        m = t;
+      }
+      const uint64_t run = ppr / g;  // lcm(ppr, 256) / 256
+      // (The division by multiply-high is exact for k = b / 8 below 2^26.)
+      if (misaligned && run >= 2 && run <= 64 && piece_blocks >= 8 * run && piece_blocks < (1ull << 29)) {
+        a.xcd_group = static_cast<uint32_t>(run);
+        a.xcd_group_magic = static_cast<uint32_t>(((1ull << 32) + run - 1) / run);
+        a.pair_limit = static_cast<uint32_t>(piece_blocks / (8 * run) * (8 * run));
+      }
+#endif
       p->kernel = reinterpret_cast<const void*>(reduce_piece_kernel<W, XF, OF, kAddrRows>);
       return hipSuccess;
     }

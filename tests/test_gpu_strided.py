@@ -112,6 +112,17 @@ def test_rows_crossing_waves_and_blocks(gpu, h, rows, out_dtype):
     _case(2, rows, h, "int8", "f32_group128", out_dtype, extra_cols=256, c0=0, seed=h + rows + 1)
 
 
+@pytest.mark.parametrize("h,rows", [(5120, 37), (7168, 70), (1152, 300), (3200, 150)])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
+def test_xcd_runs_over_whole_rows(gpu, h, rows, out_dtype):
+    # MX scale windows that start mid-line (c0 = 160 columns: 5 bytes into a
+    # scale row) make the row-strided piece launch hand each XCD runs of
+    # lcm(H/8, 256) / 256 consecutive blocks (5, 7, 9 and 25 here). These
+    # grids hold full sets of eight runs plus a tail of blocks left in
+    # hardware order: every element must still be written once, correctly.
+    _case(8, rows, h, "e4m3fn", "e8m0_block32", out_dtype, extra_cols=256, c0=160, seed=h * 7 + rows)
+
+
 @pytest.mark.parametrize("name", ["w8_bs65536_h5120_mx_e5m2_f32", "w8_bs8192_h7168_e5m2_bf16"])
 def test_full_size_row_interleaved_receive_buffer(gpu, name):
     # The W slices interleaved by row in one [rows, W, H] buffer (and the
