@@ -33,6 +33,11 @@ BASE_FLAGS = [
     "-shared",
     "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # Kernels whose leading arguments are scalars or pointers get the first
+    # 14 dwords of them preloaded into SGPRs at wave launch (the contiguous
+    # piece share, the copy, the quantize kernel); kernels whose first
+    # argument is a struct are unaffected.
+    "-Xarch_device", "-mllvm=-amdgpu-kernarg-preload-count=14",
     "-Wall",
 ]
 

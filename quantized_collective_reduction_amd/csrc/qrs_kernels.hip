@@ -117,6 +117,11 @@
 #ifndef QRS_ROWS_XCD_GROUPS
 #define QRS_ROWS_XCD_GROUPS 1
 #endif
+// The contiguous piece share: reduce_piece_flat_kernel, whose leading
+// arguments the hardware preloads (1), or reduce_piece_kernel (0).
+#ifndef QRS_PIECE_PRELOAD
+#define QRS_PIECE_PRELOAD 1
+#endif
 // The piece kernel's blocks, renumbered so that the two that share each
 // line of scales run on one XCD (see reduce_piece_kernel). 1: on; 0: off.
 #ifndef QRS_PIECE_XCD_PAIRS
@@ -764,6 +769,43 @@ __device__ __forceinline__ void store_piece_unit(const KernelArgs& a, uint64_t w
   }
 }
 
+// Converts and stores one lane's folded piece. A 16-bit output is one
+// 16-byte store at dst. An fp32 output is two 16-byte units: lane l holds
+// units 2l and 2l + 1 of the wave's 128. Trading the lower half-wave's
+// second units for the upper half-wave's first leaves lane l < 32 with
+// units 2l and 2l + 64 and lane l >= 32 with units 2l - 63 and 2l + 1: the
+// first store writes units 0..63, the second 64..127 (store_piece_unit).
+template <int OF, int ADDR>
+__device__ __forceinline__ void store_piece(const KernelArgs& a, const float (&acc)[8], u32x4* dst,
+                                            uint64_t wave_first, uint64_t n_pieces) {
+  if constexpr (OF == kOutF32) {
+    u32x4 lo, hi;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, acc[d]),
+                                                      __builtin_bit_cast(uint32_t, acc[4 + d]), false, false);
+      lo[d] = r[0];
+      hi[d] = r[1];
+    }
+    const uint32_t lane = threadIdx.x & 63u;
+    store_piece_unit<ADDR>(a, wave_first, lane < 32u ? 2u * lane : 2u * lane - 63u, n_pieces, lo);
+    store_piece_unit<ADDR>(a, wave_first, lane < 32u ? 2u * lane + 64u : 2u * lane + 1u, n_pieces, hi);
+  } else {
+    uint32_t packed[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f32x2 pr;
+      pr.x = acc[2 * k];
+      pr.y = acc[2 * k + 1];
+      if constexpr (OF == kOutBF16)
+        packed[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));  // RNE
+      else
+        packed[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, f16x2));  // RNE
+    }
+    store_stream(dst, u32x4{packed[0], packed[1], packed[2], packed[3]});
+  }
+}
+
 // Shares with MX scales: lane l of block b owns piece p = b * QRS_BLOCK + l
 // of the share, elements [8p, 8p + 8). It loads 8 code bytes per rank (one
 // 8-byte load; a wave's load covers 512 contiguous bytes of a row) and the
@@ -867,37 +909,70 @@ __global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_kernel(KernelArgs a) {
   }
   float acc[8];
   fold_piece<W, XF, SCALED>(xv, sv, acc);
+  store_piece<OF, ADDR>(a, acc, dst, wave_first, n_pieces);
+}
+
+// The contiguous form of reduce_piece_kernel (kAddrFlat32) with its hottest
+// arguments first: the piece count, the pairing bound and the W code bases
+// lead the argument list, ahead of the rest in KernelArgs (whose x[] it does
+// not read). The hardware preloads the first 14 dwords of a kernel's
+// arguments into SGPRs when the compiler is asked to
+// (-amdgpu-kernarg-preload-count), so a wave has n, the bound and x0..x5
+// when it starts: it issues those ranks' code loads at once, and makes its
+// one scalar round trip (x6, x7, the scale bases, the output) while they are
+// in flight. Piece indices and byte offsets fit 32 bits: the output, the
+// largest of the share's tensors, spans less than 4 GiB.
+template <int W, int XF, int OF>
+__global__ __launch_bounds__(QRS_BLOCK) void reduce_piece_flat_kernel(uint32_t n_pieces, uint32_t pair_limit,
+                                                                     const u32x2* x0, const u32x2* x1,
+                                                                     const u32x2* x2, const u32x2* x3,
+                                                                     const u32x2* x4, const u32x2* x5,
+                                                                     const u32x2* x6, const u32x2* x7, KernelArgs a) {
+  static_assert(XF != kXInt8, "MX scales with fp8 codes");
+  constexpr bool F32 = OF == kOutF32;
+  constexpr bool SCALED = kScaledCvt<kScaleE8M0Block32, OF>;
+  const u32x2* const xs[8] = {x0, x1, x2, x3, x4, x5, x6, x7};
+  uint32_t b = blockIdx.x;
+#if QRS_PIECE_XCD_PAIRS
+  // Pairs per XCD, as in reduce_piece_kernel.
+  if (b < pair_limit) b = (b & ~15u) | ((b & 7u) << 1) | ((b >> 3) & 1u);
+#endif
+  uint32_t p = b * QRS_BLOCK + threadIdx.x;
+  [[maybe_unused]] uint32_t wave_first = 0;
   if constexpr (F32) {
-    // Lane l holds units 2l and 2l + 1 of the wave's 128 (16 bytes each).
-    // Trading the lower half-wave's second units for the upper half-wave's
-    // first leaves lane l < 32 with units 2l and 2l + 64 and lane l >= 32
-    // with units 2l - 63 and 2l + 1: the first store writes units 0..63,
-    // the second 64..127.
-    u32x4 lo, hi;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, acc[d]),
-                                                      __builtin_bit_cast(uint32_t, acc[4 + d]), false, false);
-      lo[d] = r[0];
-      hi[d] = r[1];
-    }
-    const uint32_t lane = threadIdx.x & 63u;
-    store_piece_unit<ADDR>(a, wave_first, lane < 32u ? 2u * lane : 2u * lane - 63u, n_pieces, lo);
-    store_piece_unit<ADDR>(a, wave_first, lane < 32u ? 2u * lane + 64u : 2u * lane + 1u, n_pieces, hi);
-    return;
+    // The trade of output units needs the whole wave: lanes past the end
+    // load the last piece again and store nothing.
+    wave_first = b * QRS_BLOCK + (threadIdx.x & ~63u);
+    if (wave_first >= n_pieces) return;
+    p = p < n_pieces ? p : n_pieces - 1;
+  } else {
+    if (p >= n_pieces) return;
   }
-  uint32_t packed[4];
+  u32x2 xv[W];
+  float sv[W];
+  // The preloaded ranks' code loads first, kept ahead of everything that
+  // waits for the scalar round trip (scheduling barriers: no instruction
+  // moves across them).
+  constexpr int kPre = W < 6 ? W : 6;
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    f32x2 pr;
-    pr.x = acc[2 * k];
-    pr.y = acc[2 * k + 1];
-    if constexpr (OF == kOutBF16)
-      packed[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));  // RNE
-    else
-      packed[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, f16x2));  // RNE
-  }
-  store_stream(dst, u32x4{packed[0], packed[1], packed[2], packed[3]});
+  for (int r = 0; r < kPre; ++r)
+    xv[r] = load_stream(reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(xs[r]) + p * 8u));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = kPre; r < W; ++r)
+    xv[r] = load_stream(reinterpret_cast<const u32x2*>(reinterpret_cast<const char*>(xs[r]) + p * 8u));
+  uint32_t sb[W];
+#pragma unroll
+  for (int r = 0; r < W; ++r) sb[r] = *(static_cast<const uint8_t*>(a.scales[r]) + (p >> 2));
+  // Every load issued before the first wait for data.
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int r = 0; r < W; ++r) sv[r] = mx_scale_operand<SCALED>(sb[r]);
+  [[maybe_unused]] u32x4* dst = nullptr;
+  if constexpr (!F32) dst = reinterpret_cast<u32x4*>(static_cast<char*>(a.out[0]) + p * 16u);
+  float acc[8];
+  fold_piece<W, XF, SCALED>(xv, sv, acc);
+  store_piece<OF, kAddrFlat32>(a, acc, dst, wave_first, n_pieces);
 }
 
 // Whether a kernel instantiation takes the piece layout.
@@ -969,10 +1044,23 @@ struct Prepared {
   uint32_t blocks_per_cu_cap = 0;
   DeviceShape device{};
   KernelArgs args{};
+  // reduce_piece_flat_kernel: the leading arguments (piece count, pairing
+  // bound; the code bases come from args.x).
+  bool lead_args = false;
+  uint32_t lead_n = 0;
+  uint32_t lead_limit = 0;
 };
 
 hipError_t launch_prepared(const Prepared& p, hipStream_t stream) {
   KernelArgs a = p.args;
+  if (p.lead_args) {
+    uint32_t n = p.lead_n;
+    uint32_t limit = p.lead_limit;
+    const void* x[kMaxWorld];
+    for (int r = 0; r < kMaxWorld; ++r) x[r] = a.x[r];
+    void* arg_ptrs[] = {&n, &limit, &x[0], &x[1], &x[2], &x[3], &x[4], &x[5], &x[6], &x[7], &a};
+    return hipLaunchKernel(p.kernel, p.grid, p.block, arg_ptrs, p.lds, stream);
+  }
   void* arg_ptrs[] = {&a};
   return hipLaunchKernel(p.kernel, p.grid, p.block, arg_ptrs, p.lds, stream);
 }
@@ -1101,7 +1189,14 @@ hipError_t prepare_typed(const ReduceLaunch& l, hipStream_t stream, Prepared* p)
   if (a.chunks_per_row * OutPieces<OF>::kCount * sizeof(u32x4) < (1ull << 32)) {
     if constexpr (kPieceLayout<W, SL, OF>) {
       if (piece_blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+#if QRS_PIECE_PRELOAD
+      constexpr auto kernel = reduce_piece_flat_kernel<W, XF, OF>;
+      p->lead_args = true;
+      p->lead_n = static_cast<uint32_t>(a.total_chunks * 2);  // below 2^28: the output is under 4 GiB
+      p->lead_limit = static_cast<uint32_t>(piece_blocks) & ~15u;
+#else
       constexpr auto kernel = reduce_piece_kernel<W, XF, OF, kAddrFlat32>;
+#endif
       p->grid = dim3(static_cast<uint32_t>(piece_blocks));
       a.pair_limit = static_cast<uint32_t>(piece_blocks) & ~15u;
       p->kernel = reinterpret_cast<const void*>(kernel);
