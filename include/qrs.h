@@ -157,6 +157,37 @@ qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, 
 qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* const* scale_slices, void* out,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+typedef struct qrs_launch_s* qrs_launch_t;
+
+/*
+ * Phase 2 split in two, for callers that run the same share again and again
+ * on fixed buffers and one stream (serving loops, benchmarks): the page's
+ * two-phase interface (Prototype) carried one step further.
+ * qrs_launch_create makes every check qrs_run makes (same arguments, same
+ * errors) and chooses the kernel, grid and residency cap for the device of
+ * `stream`, then keeps them in *launch_out (host memory; no GPU work, no
+ * device allocation). qrs_launch_enqueue then enqueues that launch on that
+ * stream with no further checks: asynchronous, no host synchronisation, no
+ * allocation; the same results as qrs_run with the same arguments.
+ *
+ *   launch_out  receives the handle (non-null); NULL on error.
+ *
+ * The handle copies what it needs from the plan (which may be destroyed
+ * afterwards) but not the buffers or the stream: they must stay valid while
+ * enqueues may use them. The handle is read-only after creation, so
+ * enqueues from several threads are safe (they race on the output like any
+ * two launches on one buffer). qrs_launch_destroy frees the handle (NULL is
+ * accepted); it does not wait for enqueued work, which keeps running.
+ *
+ * qrs_launch_create returns what qrs_run returns, or QRS_ERR_OUT_OF_MEMORY;
+ * qrs_launch_enqueue returns QRS_ERR_INVALID_ARG for a NULL handle and
+ * QRS_ERR_HIP if the launch fails.
+ */
+qrs_status qrs_launch_create(qrs_plan_t plan, const void* const* x_slices, const void* const* scale_slices, void* out,
+                             void* stream, qrs_launch_t* launch_out);
+qrs_status qrs_launch_enqueue(qrs_launch_t launch);
+qrs_status qrs_launch_destroy(qrs_launch_t launch);
+
 /*
  * The whole reduce-scatter of a W-rank group computed on this GPU: every
  * rank's share, from the ranks' inputs as they are BEFORE the all-to-all.

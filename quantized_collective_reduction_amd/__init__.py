@@ -90,6 +90,9 @@ EXPORTED_SYMBOLS = (
     "qrs_last_error",
     "qrs_stream_copy",
     "qrs_run_launch_info",
+    "qrs_launch_create",
+    "qrs_launch_enqueue",
+    "qrs_launch_destroy",
 )
 
 
@@ -135,6 +138,12 @@ def load_library(path: str = LIB_PATH):
     lib.qrs_plan.restype = c_int
     lib.qrs_run.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, c_sz, vp]
     lib.qrs_run.restype = c_int
+    lib.qrs_launch_create.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, ctypes.POINTER(vp)]
+    lib.qrs_launch_create.restype = c_int
+    lib.qrs_launch_enqueue.argtypes = [vp]
+    lib.qrs_launch_enqueue.restype = c_int
+    lib.qrs_launch_destroy.argtypes = [vp]
+    lib.qrs_launch_destroy.restype = c_int
     lib.qrs_run_all_shares.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp), ctypes.POINTER(vp), vp, c_sz, vp]
     lib.qrs_run_all_shares.restype = c_int
     lib.qrs_run_strided.argtypes = [vp, ctypes.POINTER(vp), c_i64, ctypes.POINTER(vp), c_i64, vp, c_i64, vp, c_sz, vp]
@@ -424,9 +433,9 @@ def quantize(x_bf16, x_codes, scales, x_dtype, scale_layout, stream=None):
 
 
 class Launch:
-    """Arguments for ``run`` marshalled once, for repeated launches of one
-    plan on fixed buffers (each call is a single C call: no per-call Python
-    checks or array building)."""
+    """``run`` prepared once (qrs_launch_create: the checks, the kernel, grid
+    and residency cap), for repeated launches of one plan on fixed buffers
+    and one stream: each call is one qrs_launch_enqueue with one argument."""
 
     def __init__(self, p: Plan, x_slices, scale_slices, out, stream=None):
         lib = load_library()
@@ -442,21 +451,29 @@ class Launch:
         _check_plan_dtypes(p, x_slices, scale_slices, [out], "x slice", "scale slice", "out")
         self._plan = p  # keeps the plan alive
         self._keep = (list(x_slices), list(scale_slices), out)  # keeps the buffers alive
-        self._xs = (ctypes.c_void_p * w)(*[_ptr(t) for t in x_slices])
-        self._ss = (ctypes.c_void_p * w)(*[_ptr(t) for t in scale_slices])
-        self._out = ctypes.c_void_p(_ptr(out))
-        self._stream = ctypes.c_void_p(_stream_handle(stream))
-        self._fn = lib.qrs_run
-        self._handle = p.handle
+        xs = (ctypes.c_void_p * w)(*[_ptr(t) for t in x_slices])
+        ss = (ctypes.c_void_p * w)(*[_ptr(t) for t in scale_slices])
+        h = ctypes.c_void_p()
+        _check(lib.qrs_launch_create(p.handle, xs, ss, ctypes.c_void_p(_ptr(out)),
+                                     ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(h)))
+        self._h = h
+        self._destroy = lib.qrs_launch_destroy
+        self._fn = lib.qrs_launch_enqueue
 
     def on_stream(self, stream):
         """The same launch (plan and buffers) enqueued on another stream."""
         return Launch(self._plan, *self._keep, stream=stream)
 
     def __call__(self):
-        status = self._fn(self._handle, self._xs, self._ss, self._out, None, 0, self._stream)
+        status = self._fn(self._h)
         if status:
             _check(status)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._destroy(h)
+            self._h = None
 
 
 class StridedLaunch:

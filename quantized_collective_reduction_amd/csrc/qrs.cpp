@@ -12,6 +12,11 @@
 
 #include "qrs_launch.h"
 
+struct qrs_launch_s {
+  qrs::PreparedReduce* prepared;
+  hipStream_t stream;
+};
+
 struct qrs_plan_s {
   int world_size;
   int64_t bs;
@@ -159,10 +164,14 @@ qrs_status qrs_slice_pitch(qrs_plan_t plan, int full_inputs, size_t* x_pitch_out
   return ok();
 }
 
-qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* const* scale_slices, void* out,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+}  // extern "C"
+
+namespace {
+
+// The checks of qrs_run, and the launch they describe.
+qrs_status share_launch(qrs_plan_t plan, const void* const* x_slices, const void* const* scale_slices, void* out,
+                        qrs::ReduceLaunch* lp) {
+  qrs::ReduceLaunch& l = *lp;
   if (!plan) return fail(QRS_ERR_INVALID_ARG, "null plan");
   if (!x_slices || !scale_slices || !out) return fail(QRS_ERR_INVALID_ARG, "null pointer array or output");
   const int W = plan->world_size;
@@ -172,7 +181,6 @@ qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* con
   const uint64_t out_bytes = n * (plan->out_format == qrs::kOutF32 ? 4 : 2);
   if (!aligned(out, 16)) return fail(QRS_ERR_INVALID_ARG, "out is not 16-byte aligned");
 
-  qrs::ReduceLaunch l;
   std::memset(&l, 0, sizeof(l));
   l.world_size = W;
   l.x_format = plan->x_format;
@@ -192,8 +200,57 @@ qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* con
     l.x[r] = x_slices[r];
     l.scales[r] = scale_slices[r];
   }
+  return QRS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* const* scale_slices, void* out,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  qrs::ReduceLaunch l;
+  const qrs_status st = share_launch(plan, x_slices, scale_slices, out, &l);
+  if (st != QRS_OK) return st;
   const hipError_t e = qrs::launch_reduce(l, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qrs_status qrs_launch_create(qrs_plan_t plan, const void* const* x_slices, const void* const* scale_slices, void* out,
+                             void* stream, qrs_launch_t* launch_out) {
+  if (launch_out) *launch_out = nullptr;
+  if (!launch_out) return fail(QRS_ERR_INVALID_ARG, "null launch_out");
+  qrs::ReduceLaunch l;
+  const qrs_status st = share_launch(plan, x_slices, scale_slices, out, &l);
+  if (st != QRS_OK) return st;
+  qrs_launch_s* h = new (std::nothrow) qrs_launch_s;
+  if (!h) return fail(QRS_ERR_OUT_OF_MEMORY, "out of host memory");
+  h->stream = static_cast<hipStream_t>(stream);
+  const hipError_t e = qrs::prepare_reduce_launch(l, h->stream, &h->prepared);
+  if (e != hipSuccess) {
+    delete h;
+    if (e == hipErrorOutOfMemory) return fail(QRS_ERR_OUT_OF_MEMORY, "out of host memory");
+    return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
+  *launch_out = h;
+  return ok();
+}
+
+qrs_status qrs_launch_enqueue(qrs_launch_t launch) {
+  if (!launch) return fail(QRS_ERR_INVALID_ARG, "null launch");
+  const hipError_t e = qrs::enqueue_prepared_reduce(launch->prepared, launch->stream);
+  if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+qrs_status qrs_launch_destroy(qrs_launch_t launch) {
+  if (launch) {
+    qrs::destroy_prepared_reduce(launch->prepared);
+    delete launch;
+  }
   return ok();
 }
 

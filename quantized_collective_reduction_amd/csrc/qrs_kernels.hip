@@ -34,6 +34,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <new>
 
 #include "qrs_launch.h"
 
@@ -1296,6 +1297,27 @@ hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream) {
   if (e != hipSuccess) return e;
   return launch_prepared(p, stream);
 }
+
+struct PreparedReduce {
+  Prepared p;
+};
+
+hipError_t prepare_reduce_launch(const ReduceLaunch& l, hipStream_t stream, PreparedReduce** out) {
+  *out = nullptr;
+  PreparedReduce* q = new (std::nothrow) PreparedReduce;
+  if (q == nullptr) return hipErrorOutOfMemory;
+  const hipError_t e = prepare_reduce(l, stream, &q->p);
+  if (e != hipSuccess) {
+    delete q;
+    return e;
+  }
+  *out = q;
+  return hipSuccess;
+}
+
+hipError_t enqueue_prepared_reduce(const PreparedReduce* p, hipStream_t stream) { return launch_prepared(p->p, stream); }
+
+void destroy_prepared_reduce(PreparedReduce* p) { delete p; }
 
 hipError_t reduce_launch_shape(const ReduceLaunch& l, hipStream_t stream, LaunchShape* out) {
   Prepared p;

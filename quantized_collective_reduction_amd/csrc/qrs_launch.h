@@ -72,6 +72,15 @@ struct ReduceLaunch {
 // than 768 chunks.
 hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream);
 
+// launch_reduce in two steps: prepare_reduce_launch chooses the kernel, grid,
+// residency cap (for the device of `stream`) and arguments once and keeps
+// them in *out (host memory; the same errors as launch_reduce, or
+// hipErrorOutOfMemory); enqueue_prepared_reduce enqueues them on `stream`.
+struct PreparedReduce;
+hipError_t prepare_reduce_launch(const ReduceLaunch& l, hipStream_t stream, PreparedReduce** out);
+hipError_t enqueue_prepared_reduce(const PreparedReduce* p, hipStream_t stream);
+void destroy_prepared_reduce(PreparedReduce* p);
+
 // The launch device's compute-unit count and LDS sizes in bytes, as
 // hipDeviceGetAttribute reports them (multiprocessor count, shared memory per
 // multiprocessor, shared memory per block) for the device of `stream` (the

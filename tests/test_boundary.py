@@ -153,6 +153,42 @@ def test_run_rejects_bad_pointers_on_host(fake_ptr_lib):
     assert b"overlaps" in lib.qrs_last_error()
 
 
+def _create_raw(lib, p, xs, ss, out, handle):
+    w = len(xs)
+    xa = (ctypes.c_void_p * w)(*xs)
+    sa = (ctypes.c_void_p * w)(*ss)
+    return lib.qrs_launch_create(p.handle if p else None, xa, sa, out, None, handle)
+
+
+def test_prepared_launch_rejects_what_run_rejects_on_host(fake_ptr_lib):
+    # qrs_launch_create makes qrs_run's checks before it touches the GPU
+    # (these calls return before any HIP call) and leaves the handle NULL.
+    lib = fake_ptr_lib
+    p = qrs.plan(2, 32, 1024, "e4m3fn", "f32_group128", "f32")
+    n = p.rows * p.h
+    A = 1 << 40  # fake, never dereferenced
+    good_x = [A, A + (1 << 30)]
+    good_s = [A + (2 << 30), A + (3 << 30)]
+    out = A + (4 << 30)
+    h = ctypes.c_void_p(12345)
+    cases = [
+        (None, good_x, good_s, out),
+        (p, good_x, good_s, 0),
+        (p, [A, 0], good_s, out),
+        (p, [A + 8, good_x[1]], good_s, out),
+        (p, good_x, [good_s[0] + 2, good_s[1]], out),
+        (p, good_x, good_s, out + 4),
+        (p, good_x, good_s, good_x[1] + n - 16),
+    ]
+    for case in cases:
+        h.value = 12345
+        assert _create_raw(lib, *case, ctypes.byref(h)) == qrs.Status.INVALID_ARG
+        assert not h.value
+    assert _create_raw(lib, p, good_x, good_s, out, None) == qrs.Status.INVALID_ARG  # no handle pointer
+    assert lib.qrs_launch_enqueue(None) == qrs.Status.INVALID_ARG
+    assert lib.qrs_launch_destroy(None) == qrs.Status.OK
+
+
 def test_stream_copy_rejects_bad_arguments_on_host(fake_ptr_lib):
     lib = fake_ptr_lib
     A = 1 << 40
