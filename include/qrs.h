@@ -38,7 +38,7 @@
  *
  * Throughput note: one launch has a fixed cost of a few microseconds (ramp
  * up and drain); on MI355X one W=8, H=8192 MX share (172 MB) runs at about
- * 6.35 TB/s and the 514 MB W=8, H=5120 share at about 6.65 TB/s. A caller
+ * 6.4 TB/s and the 514 MB W=8, H=5120 share at about 6.7 TB/s. A caller
  * with independent shares (different batches or buckets) can alternate them
  * over two streams of the same priority to overlap the fixed cost, or hand
  * a whole group to qrs_run_all_shares (one launch).
