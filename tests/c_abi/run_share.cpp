@@ -1,6 +1,8 @@
 // A C++ caller of the C ABI with no Python in the loop: reads a problem from
 // a binary file, runs qrs_plan / qrs_run on its own HIP stream with hipMalloc'd
-// buffers, and writes the output bytes to a file.
+// buffers, and writes the output bytes to a file. It also runs the same share
+// through a prepared launch (qrs_launch_create, two qrs_launch_enqueue) into a
+// second buffer and exits with status 4 if those bytes differ.
 //
 // Input file layout (little endian): int32 W, int64 BS, int64 H, int32 x_dtype,
 // int32 scale_layout, int32 out_dtype, then W x slices [BS/W, H] (uint8), then
@@ -11,6 +13,7 @@
 
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <vector>
 
 #include "qrs.h"
@@ -75,6 +78,33 @@ int main(int argc, char** argv) {
   HIP_OK(hipStreamSynchronize(stream));
   std::vector<unsigned char> out(obytes);
   HIP_OK(hipMemcpy(out.data(), dout, obytes, hipMemcpyDeviceToHost));
+
+  // The prepared launch of the same share, enqueued twice.
+  void* dout2 = nullptr;
+  HIP_OK(hipMalloc(&dout2, obytes));
+  HIP_OK(hipMemset(dout2, 0xFF, obytes));
+  qrs_launch_t launch = nullptr;
+  st = qrs_launch_create(plan, dx.data(), ds.data(), dout2, stream, &launch);
+  if (st != QRS_OK) {
+    std::fprintf(stderr, "qrs_launch_create: %s (%s)\n", qrs_status_string(st), qrs_last_error());
+    return 3;
+  }
+  for (int k = 0; k < 2; ++k) {
+    st = qrs_launch_enqueue(launch);
+    if (st != QRS_OK) {
+      std::fprintf(stderr, "qrs_launch_enqueue: %s (%s)\n", qrs_status_string(st), qrs_last_error());
+      return 3;
+    }
+  }
+  HIP_OK(hipStreamSynchronize(stream));
+  qrs_launch_destroy(launch);
+  std::vector<unsigned char> out2(obytes);
+  HIP_OK(hipMemcpy(out2.data(), dout2, obytes, hipMemcpyDeviceToHost));
+  HIP_OK(hipFree(dout2));
+  if (std::memcmp(out.data(), out2.data(), obytes) != 0) {
+    std::fprintf(stderr, "prepared launch differs from qrs_run\n");
+    return 4;
+  }
 
   FILE* g = std::fopen(argv[2], "wb");
   if (!g || std::fwrite(out.data(), 1, obytes, g) != obytes) return 1;
