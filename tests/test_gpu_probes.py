@@ -77,25 +77,29 @@ def test_worked_example_on_gpu(gpu, ex):
     assert np.all(got == want), (ex["name"], hex(int(got.ravel()[0])), hex(want))
 
 
+@pytest.mark.parametrize("w", [2, 8])
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("x_format", ["e4m3fn", "e5m2"])
-def test_every_code_times_every_e8m0_code(gpu, x_format, out_dtype):
-    # All 256 x 256 (x code, E8M0 code) pairs through the MX kernel: element i
-    # holds x code i % 256 under scale code i // 256. Rank 1 adds -0 (code
-    # 0x80), which leaves every product unchanged, so the output is the
-    # product itself: the IEEE binary32 product of the two decoded values,
-    # bit for bit (2^-127 for code 0, NaN for 255, overflow to infinity,
-    # subnormal results, signed zeros). fp32 outputs take the scaled fp8
-    # conversions, 16-bit outputs decode and multiply: both are checked.
+def test_every_code_times_every_e8m0_code(gpu, x_format, out_dtype, w):
+    # All 256 x 256 (x code, E8M0 code) pairs through the MX kernels: element
+    # i holds x code i % 256 under scale code i // 256. The other ranks add
+    # -0 (code 0x80), which leaves every product unchanged, so the output is
+    # the product itself: the IEEE binary32 product of the two decoded
+    # values, bit for bit (2^-127 for code 0, NaN for 255, overflow to
+    # infinity, subnormal results, signed zeros). fp32 outputs take the
+    # scaled fp8 conversions, 16-bit outputs decode and multiply: both are
+    # checked, at W = 2 (fp32: 16-element chunks) and W = 8 (8-element
+    # pieces for both outputs).
     rows, h = 8, 8192
     codes = np.tile(np.arange(256, dtype=np.uint8), rows * h // 256).reshape(rows, h)
     neg_zero = np.full((rows, h), 0x80, dtype=np.uint8)
     r_idx, b_idx = np.meshgrid(np.arange(rows), np.arange(h // 32), indexing="ij")
     scale_codes = (r_idx * (h // 256) + b_idx // 8).astype(np.uint8)  # element i -> i // 256
     unit = np.full((rows, h // 32), 127, dtype=np.uint8)
-    got = run_gpu(2, rows, h, x_format, "e8m0_block32", out_dtype, [codes, neg_zero], [scale_codes, unit])
-    want_o = oracle_bits(oracle.reduce_scatter_share([codes, neg_zero], [scale_codes, unit], x_format,
-                                                     "e8m0_block32", out_dtype), out_dtype)
+    xs = [codes] + [neg_zero] * (w - 1)
+    ss = [scale_codes] + [unit] * (w - 1)
+    got = run_gpu(w, rows, h, x_format, "e8m0_block32", out_dtype, xs, ss)
+    want_o = oracle_bits(oracle.reduce_scatter_share(xs, ss, x_format, "e8m0_block32", out_dtype), out_dtype)
     assert_parity(got, want_o, out_dtype, f"{x_format} x E8M0 -> {out_dtype}")
     if out_dtype != "f32":
         return
