@@ -25,10 +25,11 @@
 // and scale in one scaled conversion instead (exact, see product_pair).
 // fp32 outputs go through LDS and 16-bit outputs with fp32 group scales
 // through a cross-half lane swap, so that each store instruction writes one
-// contiguous 1 KiB. MX modes with 16-bit outputs get the same from lanes
-// that own 8 elements (a "piece": one 8-byte load per rank, one 16-byte
-// store) in the contiguous share. Which variant each mode uses was chosen by
-// measurement; the macros below select them.
+// contiguous 1 KiB. MX modes with 16-bit outputs, and with fp32 outputs at
+// W = 4 and 8, get the same from lanes that own 8 elements instead (a
+// "piece": one 8-byte load per rank, one 16-byte store per 16-bit piece,
+// two swapped ones per fp32 piece), in every launch form. Which variant
+// each mode uses was chosen by measurement; the macros below select them.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -409,7 +410,9 @@ __device__ __forceinline__ void pack_chunk(const float (&acc)[kChunk], u32x4 (&p
 // wave and it waits once for them, instead of once for the bounds and
 // again, after the bounds check, for the base pointers. Measured about 1 %
 // faster on the W=8 H=8192 piece kernel, whose waves are short-lived, and
-// about 0.35 % on the W=8 H=5120 chunk kernel. One asm statement per group:
+// about 0.35 % on the W=8 H=5120 share in 16-element chunks (the contiguous
+// piece share now preloads its leading arguments instead; see
+// reduce_piece_flat_kernel). One asm statement per group:
 // separate statements let the scheduler put a wait between them.
 template <int W>
 __device__ __forceinline__ void pin_flat_args(const KernelArgs& a, uint64_t n, uint32_t m);
