@@ -82,3 +82,31 @@ def test_quantize_then_all_shares_in_one_graph(gpu):
     for c in codes:
         c.zero_()  # the replay must also redo the quantization
     _replay_and_check(g, outs, want_bits, float("nan"))
+
+
+@pytest.mark.parametrize("name", ["w8_bs16384_h8192_mx_e4m3_bf16", "w8_bs65536_h5120_mx_e5m2_f32"])
+def test_prepared_launch_in_a_graph(gpu, name):
+    """A prepared launch (qrs_launch_create on the capture stream) captured
+    twice in one graph: the contiguous piece kernel with preloaded
+    arguments, 16-bit and fp32 outputs."""
+    wl = workloads.WORKLOADS[name].with_(bs=8 * 48)
+    xs, ss = workloads.generate(wl)
+    p = qrs.plan(8, wl.bs, wl.h, wl.x_format, wl.scale_layout, wl.out_dtype)
+    dx, ds = qrs.alloc_slices(p)
+    for t, a in zip(dx, xs):
+        t.copy_(torch.from_numpy(a))
+    for t, a in zip(ds, ss):
+        t.copy_(torch.from_numpy(a))
+    out = empty_out(wl.rows, wl.h, wl.out_dtype)
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, wl.x_format, wl.scale_layout, wl.out_dtype), wl.out_dtype)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    launch = qrs.Launch(p, dx, ds, out, stream=s)
+    launch()  # warm-up on the capture stream
+    torch.cuda.synchronize()
+    assert_parity(out_bits(out), want, wl.out_dtype, "eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        launch()
+        launch()
+    _replay_and_check(g, [out], [want.view(np.uint8).reshape(wl.rows, -1)], float("nan"))
