@@ -19,9 +19,9 @@ Prints ONE JSON line on stdout:
                    average launch duration (HIP events recorded on the launch
                    stream at both ends of the K timed launches, divided by
                    K), against the 8 TB/s HBM peak. For --op all_shares one
-                   step is one qrs_run_all_shares call: one launch up to about
-                   300 MB per share, W launches (one per share) above, so
-                   kernel_us_avg is then per call and achieved is unchanged;
+                   step is one qrs_run_all_shares call: one launch, or W
+                   (one per share) for uncapped layouts past about 300 MB per
+                   share, so kernel_us_avg is per call;
                    traffic = measured HBM bytes per launch from committed
                    rocprofv3 counter summaries, when they match this kernel
                    source (else null);

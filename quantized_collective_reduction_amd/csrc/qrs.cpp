@@ -322,14 +322,17 @@ qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const 
     l.x[r] = x_full[r];
     l.scales[r] = scale_full[r];
   }
-  // Large shares run as one launch each: past about 300 MB of algorithmic
-  // bytes per share that measured faster than one launch over all shares
-  // (514 MB per share: 639 us against 672 us for the group), while smaller
-  // shares gain from sharing one launch's fixed cost (172 MB per share: 220
-  // us against 231 us). Both give the same bits.
+  // Large shares of the uncapped launches run as one launch each: past about
+  // 300 MB of algorithmic bytes per share that measured faster than one
+  // launch over all shares (514 MB per share with fp32 group scales: 640
+  // against 671 us for the group; MX at W = 2: 156 against 173 us), while
+  // smaller shares gain from sharing one launch's fixed cost (172 MB per
+  // share: 207 against 223 us). Groups that run as capped 8-element pieces
+  // (MX at W = 8) stay one launch at any size (514 MB per share: 607 against
+  // 614 us). Both give the same bits.
   const uint64_t share_bytes = n * static_cast<uint64_t>(W) + share_scale_bytes * static_cast<uint64_t>(W) + out_bytes;
   hipError_t e = hipSuccess;
-  if (share_bytes > kSplitShareBytes) {
+  if (share_bytes > kSplitShareBytes && !qrs::all_shares_take_one_capped_launch(l)) {
     qrs::ReduceLaunch one = l;
     one.n_shares = 1;
     for (int j = 0; j < W && e == hipSuccess; ++j) {

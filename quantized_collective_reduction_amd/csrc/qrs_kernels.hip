@@ -1294,6 +1294,31 @@ bool device_shape(hipStream_t stream, DeviceShape* out) {
   return true;
 }
 
+namespace {
+template <int W, int SL, int OF>
+constexpr bool kSharesOneCappedLaunch = kPieceLayout<W, SL, OF> && kPieceSharesBlocksPerCu<W> > 0;
+
+template <int W>
+bool shares_one_capped_launch_w(const ReduceLaunch& l) {
+  if (l.scale_layout != kScaleE8M0Block32) return false;
+  switch (l.out_format) {
+    case kOutF32: return kSharesOneCappedLaunch<W, kScaleE8M0Block32, kOutF32>;
+    case kOutBF16: return kSharesOneCappedLaunch<W, kScaleE8M0Block32, kOutBF16>;
+    case kOutF16: return kSharesOneCappedLaunch<W, kScaleE8M0Block32, kOutF16>;
+  }
+  return false;
+}
+}  // namespace
+
+bool all_shares_take_one_capped_launch(const ReduceLaunch& l) {
+  switch (l.world_size) {
+    case 2: return shares_one_capped_launch_w<2>(l);
+    case 4: return shares_one_capped_launch_w<4>(l);
+    case 8: return shares_one_capped_launch_w<8>(l);
+  }
+  return false;
+}
+
 hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream) {
   Prepared p;
   const hipError_t e = prepare_reduce(l, stream, &p);

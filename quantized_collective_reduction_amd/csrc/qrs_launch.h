@@ -72,6 +72,11 @@ struct ReduceLaunch {
 // than 768 chunks.
 hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream);
 
+// Whether an all-shares launch of this mode (n_shares = world_size) runs as
+// 8-element pieces with a residency cap: such groups measured faster as one
+// launch even where their shares are large.
+bool all_shares_take_one_capped_launch(const ReduceLaunch& l);
+
 // launch_reduce in two steps: prepare_reduce_launch chooses the kernel, grid,
 // residency cap (for the device of `stream`) and arguments once and keeps
 // them in *out (host memory; the same errors as launch_reduce, or

@@ -102,3 +102,39 @@ def test_all_shares_large_shares_one_launch_each(gpu):
         qrs.run(p, dx, ds, out)
         torch.cuda.synchronize()
         assert np.array_equal(out_bits(out), got[j]), f"share {j}"
+
+
+def test_all_shares_large_capped_group_one_launch(gpu):
+    """A W=8 MX group runs as one capped launch of 8-element pieces even
+    where its shares are large: W=8, BS=24576, H=8192 MX E5M2 -> fp32 is 309
+    MB per share (2.5 GB for the group). The inputs are drawn on the GPU
+    (finite codes, E8M0 bytes 112..142); every share must equal qrs_run on
+    its row blocks, byte for byte, and 16 sampled rows must match the
+    oracle."""
+    w, rows, h = 8, 3072, 8192
+    bs = w * rows
+    p = qrs.plan(w, bs, h, "e5m2", "e8m0_block32", "f32")
+    per_share = w * rows * h + w * rows * h // 32 + rows * h * 4
+    assert per_share > 300_000_000
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    xs = []
+    for _ in range(w):
+        mag = torch.randint(0, 124, (bs, h), dtype=torch.int32, device="cuda", generator=gen)
+        sign = torch.randint(0, 2, (bs, h), dtype=torch.int32, device="cuda", generator=gen) << 7
+        xs.append((mag | sign).to(torch.uint8))
+    ss = [torch.randint(112, 143, (bs, h // 32), dtype=torch.int32, device="cuda", generator=gen).to(torch.uint8)
+          for _ in range(w)]
+    outs = [empty_out(rows, h, "f32").fill_(float("nan")) for _ in range(w)]
+    log("[all_shares] one launch over a 2.5 GB W=8 group")
+    qrs.run_all_shares(p, xs, ss, outs)
+    torch.cuda.synchronize()
+    sample = np.sort(np.concatenate([[0, rows - 1], np.random.default_rng(3).choice(rows, 14, replace=False)]))
+    ref = empty_out(rows, h, "f32")
+    for j in range(w):
+        qrs.run(p, [x[j * rows:(j + 1) * rows] for x in xs], [s[j * rows:(j + 1) * rows] for s in ss], ref)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[j].view(torch.uint8), ref.view(torch.uint8)), f"share {j}"
+        rx = [x[j * rows:(j + 1) * rows][sample].cpu().numpy() for x in xs]
+        rs = [s[j * rows:(j + 1) * rows][sample].cpu().numpy() for s in ss]
+        want = oracle.reduce_scatter_share(rx, rs, "e5m2", "e8m0_block32", "f32")
+        assert_parity(out_bits(outs[j])[sample], oracle_bits(want, "f32"), "f32", f"share {j} sampled rows")
