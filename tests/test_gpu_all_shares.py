@@ -138,3 +138,68 @@ def test_all_shares_large_capped_group_one_launch(gpu):
         rs = [s[j * rows:(j + 1) * rows][sample].cpu().numpy() for s in ss]
         want = oracle.reduce_scatter_share(rx, rs, "e5m2", "e8m0_block32", "f32")
         assert_parity(out_bits(outs[j])[sample], oracle_bits(want, "f32"), "f32", f"share {j} sampled rows")
+
+
+def _gpu_codes(x_format, shape, gen):
+    """Random finite codes of the format, drawn on the GPU."""
+    b = torch.randint(0, 256, shape, dtype=torch.int32, device="cuda", generator=gen)
+    if x_format == "e4m3fn":
+        b = torch.where((b & 0x7F) == 0x7F, b - 1, b)  # no NaN
+    elif x_format == "e5m2":
+        b = torch.where((b & 0x7F) >= 0x7C, b & 0x83, b)  # no inf or NaN
+    return b.to(torch.uint8)
+
+
+def _gpu_scales(scale_layout, shape, gen):
+    if scale_layout == "e8m0_block32":
+        return torch.randint(112, 143, shape, dtype=torch.int32, device="cuda", generator=gen).to(torch.uint8)
+    e = torch.randint(-14, 3, shape, dtype=torch.int32, device="cuda", generator=gen).float()
+    m = 1.0 + torch.rand(shape, device="cuda", generator=gen)
+    return (m * torch.exp2(e)).to(torch.float32)
+
+
+def _large_group_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        xf, sl = MODES[rng.integers(len(MODES))]
+        out.append(dict(w=int(rng.choice([2, 4, 8])), rows=int(rng.integers(100, 701)),
+                        h=int(128 * rng.integers(8, 65)), x_format=xf, scale_layout=sl,
+                        out_dtype=str(rng.choice(["f32", "bf16", "f16"]))))
+    return out
+
+
+LARGE_GROUP_CASES = _large_group_cases(12, 515) + [
+    dict(w=8, rows=400, h=4096, x_format="e4m3fn", scale_layout="e8m0_block32", out_dtype="bf16"),  # capped
+    dict(w=8, rows=300, h=7168, x_format="e5m2", scale_layout="e8m0_block32", out_dtype="f32"),  # capped
+]
+
+
+@pytest.mark.parametrize("c", LARGE_GROUP_CASES,
+                         ids=lambda c: f"W{c['w']}-r{c['rows']}-h{c['h']}-{c['x_format']}-{c['scale_layout']}-"
+                                       f"{c['out_dtype']}")
+def test_all_shares_random_larger_groups(gpu, c):
+    """Groups of 100 to 700 rows per share (at W = 8 past three generations
+    of capped blocks, so the capped launch runs), inputs drawn on the GPU:
+    every share equals qrs_run on its row blocks, byte for byte, and
+    sampled rows of two shares match the oracle."""
+    w, rows, h = c["w"], c["rows"], c["h"]
+    xf, sl, od = c["x_format"], c["scale_layout"], c["out_dtype"]
+    g = 128 if sl == "f32_group128" else 32
+    gen = torch.Generator(device="cuda").manual_seed(rows * 131 + h)
+    xs = [_gpu_codes(xf, (w * rows, h), gen) for _ in range(w)]
+    ss = [_gpu_scales(sl, (w * rows, h // g), gen) for _ in range(w)]
+    p = qrs.plan(w, w * rows, h, xf, sl, od)
+    outs = [empty_out(rows, h, od).fill_(float("nan")) for _ in range(w)]
+    qrs.run_all_shares(p, xs, ss, outs)
+    ref = empty_out(rows, h, od)
+    sample = np.array([0, rows // 3, rows - 1])
+    for j in range(w):
+        qrs.run(p, [x[j * rows:(j + 1) * rows] for x in xs], [s[j * rows:(j + 1) * rows] for s in ss], ref)
+        torch.cuda.synchronize()
+        assert torch.equal(outs[j].view(torch.uint8), ref.view(torch.uint8)), f"share {j}"
+        if j in (0, w - 1):
+            rx = [x[j * rows:(j + 1) * rows][sample].cpu().numpy() for x in xs]
+            rs = [s[j * rows:(j + 1) * rows][sample].cpu().numpy() for s in ss]
+            want = oracle.reduce_scatter_share(rx, rs, xf, sl, od)
+            assert_parity(out_bits(outs[j])[sample], oracle_bits(want, od), od, f"share {j} sampled rows")
