@@ -149,10 +149,19 @@ qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, 
  *                 unused (the plan needs none); any value is accepted.
  *   stream        a hipStream_t (NULL = the default stream).
  *
+ * A share of more than 2^34 elements runs as consecutive launches over
+ * consecutive 2^34-element ranges (a HIP grid holds fewer than 2^32
+ * work-items along a dimension); the results are the same bits as one
+ * launch's. The environment variable QRS_MAX_LAUNCH_ELEMS, read once per
+ * process, may lower that bound to a multiple of 4096 elements (this and
+ * every other call that launches reduce or quantize kernels); any other
+ * value makes those calls return QRS_ERR_INVALID_ARG.
+ *
  * Returns QRS_ERR_INVALID_ARG for a null plan or pointer, a misaligned
- * pointer or an output that overlaps an input, and QRS_ERR_HIP if the kernel
- * launch fails. Inputs are not validated element by element: NaN or
- * infinite codes and scales propagate as in IEEE 754.
+ * pointer or an output that overlaps an input, and QRS_ERR_HIP if a kernel
+ * launch fails (every launch of a split share is checked before the first is
+ * enqueued). Inputs are not validated element by element: NaN or infinite
+ * codes and scales propagate as in IEEE 754.
  */
 qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* const* scale_slices, void* out,
                    void* workspace, size_t workspace_bytes, void* stream);
@@ -165,8 +174,9 @@ typedef struct qrs_launch_s* qrs_launch_t;
  * two-phase interface (Prototype) carried one step further.
  * qrs_launch_create makes every check qrs_run makes (same arguments, same
  * errors) and chooses the kernel, grid and residency cap for the device of
- * `stream`, then keeps them in *launch_out (host memory; no GPU work, no
- * device allocation). qrs_launch_enqueue then enqueues that launch on that
+ * `stream` (for each launch of a share split as qrs_run splits it), then
+ * keeps them in *launch_out (host memory; no GPU work, no device
+ * allocation). qrs_launch_enqueue then enqueues that launch on that
  * stream with no further checks: asynchronous, no host synchronisation, no
  * allocation; the same results as qrs_run with the same arguments.
  *
@@ -202,8 +212,9 @@ qrs_status qrs_launch_destroy(qrs_launch_t launch);
  * with the same arithmetic as qrs_run. Up to about 300 MB of algorithmic
  * bytes per share one launch covers all W shares; larger shares are
  * enqueued as W launches, one per share, on the same stream (measured
- * faster on MI355X at those sizes). Either way the call only enqueues work,
- * and the results are the same.
+ * faster on MI355X at those sizes). Shares of more than 2^34 elements are
+ * further split into launches over element ranges, as qrs_run splits them.
+ * Either way the call only enqueues work, and the results are the same.
  *
  *   x_full        HOST array of W DEVICE pointers; x_full[r] is rank r's
  *                 uint8 codes [BS, H], contiguous, 16-byte aligned.
@@ -238,9 +249,11 @@ qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const 
  *
  * Each row stride, in bytes, must be below 4 GiB, the plan's rows per
  * share below 2^32, and one slice's scales, from its first row's start to
- * its last row's end, must span less than 4 GiB. The output's address span, from its first to the last
- * element written, must not overlap the address span of any input slice.
- * Errors as for qrs_run.
+ * its last row's end, must span less than 4 GiB. The output's address span,
+ * from its first to the last element written, must not overlap the address
+ * span of any input slice. A share of more than 2^34 elements runs as
+ * launches over consecutive row ranges of at most 2^34 elements (at least
+ * one row each), as qrs_run splits contiguous shares. Errors as for qrs_run.
  */
 qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t x_row_stride,
                            const void* const* scale_slices, int64_t scale_row_stride, void* out,
@@ -277,6 +290,8 @@ qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t
  *   stream      a hipStream_t (NULL = the default stream).
  *
  * The three buffers must not overlap. Asynchronous; allocates nothing.
+ * More than 2^34 elements run as consecutive launches over 2^34-element
+ * ranges, under the same bound as qrs_run (QRS_MAX_LAUNCH_ELEMS included).
  */
 qrs_status qrs_quantize(int64_t tokens, int64_t h, qrs_x_dtype x_dtype, qrs_scale_layout scale_layout,
                         const void* x_bf16, void* x_codes, void* scales, void* stream);
@@ -319,6 +334,10 @@ qrs_status qrs_slice_pitch(qrs_plan_t plan, int full_inputs, size_t* x_pitch_out
  * anything. Host only; the library reads the device's sizes with
  * hipDeviceGetAttribute (once per device) but enqueues no work.
  *
+ *   launches           kernel launches qrs_run makes: 1, or more for shares
+ *                      of more than 2^34 elements (see qrs_run); the other
+ *                      fields describe the first launch, and every launch
+ *                      but the last is alike;
  *   blocks             work-groups in the grid;
  *   threads_per_block  threads per work-group;
  *   dynamic_lds_bytes  unused LDS requested per work-group so that at most
@@ -340,6 +359,7 @@ typedef struct qrs_launch_info {
   uint32_t device_cus;
   uint32_t device_lds_per_cu;
   uint32_t device_lds_per_block;
+  uint32_t launches;
 } qrs_launch_info;
 
 qrs_status qrs_run_launch_info(qrs_plan_t plan, void* stream, qrs_launch_info* info_out);
@@ -356,7 +376,8 @@ const char* qrs_last_error(void);
  * `stream` with the same 16-byte streaming loads and stores the reduction
  * uses. It is the reference stream for bandwidth and traffic-counter
  * calibration. bytes must be a positive multiple of 16, both pointers
- * 16-byte aligned device pointers, and the ranges must not overlap.
+ * 16-byte aligned device pointers, and the ranges must not overlap. More
+ * than 2^35 bytes run as consecutive launches of 2^35 bytes.
  */
 qrs_status qrs_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
 

@@ -107,6 +107,7 @@ class LaunchInfo(ctypes.Structure):
         ("device_cus", ctypes.c_uint32),
         ("device_lds_per_cu", ctypes.c_uint32),
         ("device_lds_per_block", ctypes.c_uint32),
+        ("launches", ctypes.c_uint32),
     ]
 
     def as_dict(self):

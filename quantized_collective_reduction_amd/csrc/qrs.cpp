@@ -5,16 +5,19 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <cerrno>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 
 #include "qrs_launch.h"
 
 struct qrs_launch_s {
-  qrs::PreparedReduce* prepared;
   hipStream_t stream;
+  uint64_t n_parts;
+  qrs::PreparedReduce** parts;  // n_parts launches, enqueued in this order
 };
 
 struct qrs_plan_s {
@@ -77,6 +80,99 @@ bool valid_h(int64_t h) { return h >= 1024 && h <= 8192 && h % 128 == 0; }
 
 qrs::XFormat to_x_format(qrs_x_dtype x) {
   return x == QRS_X_INT8 ? qrs::kXInt8 : x == QRS_X_FP8_E4M3FN ? qrs::kXE4M3FN : qrs::kXE5M2;
+}
+
+// HIP runs at most 2^32 - 1 work-items along a grid dimension, and every
+// kernel gives a lane at least 8 elements. A call over more elements per
+// share than one launch may cover (kMaxLaunchElems) therefore runs as
+// consecutive launches over consecutive element ranges of each share (whole
+// rows of a row-strided share). Each launch computes its elements exactly as
+// one launch over the whole share would, so the results are the same bits.
+// QRS_MAX_LAUNCH_ELEMS, read once per process, may lower the bound (a
+// multiple of 4096 elements), which runs the same split at small sizes; any
+// other value makes every call that launches fail with QRS_ERR_INVALID_ARG.
+constexpr uint64_t kMaxLaunchElems = uint64_t{1} << 34;  // 2^31 lanes of 8 elements
+constexpr uint64_t kMaxCopyBytes = uint64_t{1} << 35;    // 2^31 lanes of 16 bytes
+
+uint64_t max_launch_elems() {
+  static const uint64_t bound = [] {
+    const char* s = std::getenv("QRS_MAX_LAUNCH_ELEMS");
+    if (s == nullptr || *s == '\0') return kMaxLaunchElems;
+    char* end = nullptr;
+    errno = 0;
+    const unsigned long long v = std::strtoull(s, &end, 10);
+    if (errno != 0 || *end != '\0' || s[0] < '0' || s[0] > '9' || v < 4096 || v > kMaxLaunchElems || v % 4096 != 0)
+      return uint64_t{0};
+    return static_cast<uint64_t>(v);
+  }();
+  return bound;
+}
+
+qrs_status check_launch_bound() {
+  if (max_launch_elems() == 0)
+    return fail(QRS_ERR_INVALID_ARG, "QRS_MAX_LAUNCH_ELEMS must be a multiple of 4096 in [4096, 2^34]");
+  return QRS_OK;
+}
+
+// Rows per launch of a row-strided share (at least one).
+uint64_t part_rows(const qrs::ReduceLaunch& l, uint64_t m) {
+  const uint64_t r = m / l.row_elems;
+  return r != 0 ? r : 1;
+}
+
+uint64_t part_count(const qrs::ReduceLaunch& l, uint64_t m) {
+  if (l.n_rows > 1) {
+    const uint64_t r = part_rows(l, m);
+    return (l.n_rows + r - 1) / r;
+  }
+  return (l.row_elems + m - 1) / m;
+}
+
+// Launch k of l's split. Contiguous shares (n_rows = 1, all shares of a
+// group alike): elements [k m, k m + m) of every share, whose scales start
+// k m / 32 bytes further on in both layouts (4 bytes per 128 elements, or 1
+// per 32); the share strides stay. Row-strided shares: rows [k R, k R + R).
+qrs::ReduceLaunch part_of(const qrs::ReduceLaunch& l, uint64_t m, uint64_t k) {
+  qrs::ReduceLaunch q = l;
+  const uint64_t ob = l.out_format == qrs::kOutF32 ? 4 : 2;
+  uint64_t dx, ds, dout;
+  if (l.n_rows > 1) {
+    const uint64_t r = part_rows(l, m), r0 = k * r;
+    q.n_rows = l.n_rows - r0 < r ? l.n_rows - r0 : r;
+    dx = r0 * l.x_row_stride;
+    ds = r0 * l.scale_row_stride;
+    dout = r0 * l.out_row_stride;
+  } else {
+    const uint64_t e0 = k * m;
+    q.row_elems = l.row_elems - e0 < m ? l.row_elems - e0 : m;
+    dx = e0;
+    ds = e0 / 32;
+    dout = e0 * ob;
+  }
+  for (int r = 0; r < l.world_size; ++r) {
+    q.x[r] = static_cast<const char*>(l.x[r]) + dx;
+    q.scales[r] = static_cast<const char*>(l.scales[r]) + ds;
+  }
+  for (int j = 0; j < l.n_shares; ++j) q.out[j] = static_cast<char*>(l.out[j]) + dout;
+  return q;
+}
+
+// Enqueues l as its launches, in order, after checking every one of them.
+hipError_t launch_in_parts(const qrs::ReduceLaunch& l, hipStream_t stream) {
+  const uint64_t m = max_launch_elems();
+  if (m == 0) return hipErrorInvalidValue;  // callers report check_launch_bound() first
+  const uint64_t parts = part_count(l, m);
+  if (parts == 1) return qrs::launch_reduce(l, stream);
+  for (uint64_t k = 0; k < parts; ++k) {
+    qrs::LaunchShape shape;
+    const hipError_t e = qrs::reduce_launch_shape(part_of(l, m, k), stream, &shape);
+    if (e != hipSuccess) return e;
+  }
+  for (uint64_t k = 0; k < parts; ++k) {
+    const hipError_t e = qrs::launch_reduce(part_of(l, m, k), stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace
@@ -212,9 +308,11 @@ qrs_status qrs_run(qrs_plan_t plan, const void* const* x_slices, const void* con
   (void)workspace;
   (void)workspace_bytes;
   qrs::ReduceLaunch l;
-  const qrs_status st = share_launch(plan, x_slices, scale_slices, out, &l);
+  qrs_status st = share_launch(plan, x_slices, scale_slices, out, &l);
   if (st != QRS_OK) return st;
-  const hipError_t e = qrs::launch_reduce(l, static_cast<hipStream_t>(stream));
+  st = check_launch_bound();
+  if (st != QRS_OK) return st;
+  const hipError_t e = launch_in_parts(l, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -224,16 +322,27 @@ qrs_status qrs_launch_create(qrs_plan_t plan, const void* const* x_slices, const
   if (launch_out) *launch_out = nullptr;
   if (!launch_out) return fail(QRS_ERR_INVALID_ARG, "null launch_out");
   qrs::ReduceLaunch l;
-  const qrs_status st = share_launch(plan, x_slices, scale_slices, out, &l);
+  qrs_status st = share_launch(plan, x_slices, scale_slices, out, &l);
   if (st != QRS_OK) return st;
+  st = check_launch_bound();
+  if (st != QRS_OK) return st;
+  const uint64_t m = max_launch_elems();
   qrs_launch_s* h = new (std::nothrow) qrs_launch_s;
   if (!h) return fail(QRS_ERR_OUT_OF_MEMORY, "out of host memory");
   h->stream = static_cast<hipStream_t>(stream);
-  const hipError_t e = qrs::prepare_reduce_launch(l, h->stream, &h->prepared);
-  if (e != hipSuccess) {
+  h->n_parts = part_count(l, m);
+  h->parts = new (std::nothrow) qrs::PreparedReduce*[h->n_parts]();
+  if (!h->parts) {
     delete h;
-    if (e == hipErrorOutOfMemory) return fail(QRS_ERR_OUT_OF_MEMORY, "out of host memory");
-    return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return fail(QRS_ERR_OUT_OF_MEMORY, "out of host memory");
+  }
+  for (uint64_t k = 0; k < h->n_parts; ++k) {
+    const hipError_t e = qrs::prepare_reduce_launch(part_of(l, m, k), h->stream, &h->parts[k]);
+    if (e != hipSuccess) {
+      qrs_launch_destroy(h);
+      if (e == hipErrorOutOfMemory) return fail(QRS_ERR_OUT_OF_MEMORY, "out of host memory");
+      return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    }
   }
   *launch_out = h;
   return ok();
@@ -241,14 +350,18 @@ qrs_status qrs_launch_create(qrs_plan_t plan, const void* const* x_slices, const
 
 qrs_status qrs_launch_enqueue(qrs_launch_t launch) {
   if (!launch) return fail(QRS_ERR_INVALID_ARG, "null launch");
-  const hipError_t e = qrs::enqueue_prepared_reduce(launch->prepared, launch->stream);
-  if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  for (uint64_t k = 0; k < launch->n_parts; ++k) {
+    const hipError_t e = qrs::enqueue_prepared_reduce(launch->parts[k], launch->stream);
+    if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 
 qrs_status qrs_launch_destroy(qrs_launch_t launch) {
   if (launch) {
-    qrs::destroy_prepared_reduce(launch->prepared);
+    for (uint64_t k = 0; k < launch->n_parts; ++k)
+      if (launch->parts[k]) qrs::destroy_prepared_reduce(launch->parts[k]);
+    delete[] launch->parts;
     delete launch;
   }
   return ok();
@@ -265,9 +378,13 @@ qrs_status qrs_run_launch_info(qrs_plan_t plan, void* stream, qrs_launch_info* i
   l.n_rows = 1;
   l.row_elems = static_cast<uint64_t>(plan->rows) * static_cast<uint64_t>(plan->h);
   l.n_shares = 1;
+  const qrs_status st = check_launch_bound();
+  if (st != QRS_OK) return st;
+  const uint64_t m = max_launch_elems();
   qrs::LaunchShape shape;
-  const hipError_t e = qrs::reduce_launch_shape(l, static_cast<hipStream_t>(stream), &shape);
+  const hipError_t e = qrs::reduce_launch_shape(part_of(l, m, 0), static_cast<hipStream_t>(stream), &shape);
   if (e != hipSuccess) return fail(QRS_ERR_HIP, "launch shape: %s", hipGetErrorString(e));
+  info_out->launches = static_cast<uint32_t>(part_count(l, m));  // at most 2^40 / 4096
   info_out->blocks = shape.blocks;
   info_out->threads_per_block = shape.threads_per_block;
   info_out->dynamic_lds_bytes = shape.dynamic_lds;
@@ -331,6 +448,8 @@ qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const 
   // (MX at W = 8) stay one launch at any size (514 MB per share: 607 against
   // 614 us). Both give the same bits.
   const uint64_t share_bytes = n * static_cast<uint64_t>(W) + share_scale_bytes * static_cast<uint64_t>(W) + out_bytes;
+  const qrs_status st = check_launch_bound();
+  if (st != QRS_OK) return st;
   hipError_t e = hipSuccess;
   if (share_bytes > kSplitShareBytes && !qrs::all_shares_take_one_capped_launch(l)) {
     qrs::ReduceLaunch one = l;
@@ -342,10 +461,10 @@ qrs_status qrs_run_all_shares(qrs_plan_t plan, const void* const* x_full, const 
       }
       for (int k = 0; k < qrs::kMaxWorld; ++k) one.out[k] = nullptr;
       one.out[0] = out_shares[j];
-      e = qrs::launch_reduce(one, static_cast<hipStream_t>(stream));
+      e = launch_in_parts(one, static_cast<hipStream_t>(stream));
     }
   } else {
-    e = qrs::launch_reduce(l, static_cast<hipStream_t>(stream));
+    e = launch_in_parts(l, static_cast<hipStream_t>(stream));
   }
   if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -417,7 +536,9 @@ qrs_status qrs_run_strided(qrs_plan_t plan, const void* const* x_slices, int64_t
     l.x[r] = x_slices[r];
     l.scales[r] = scale_slices[r];
   }
-  const hipError_t e = qrs::launch_reduce(l, static_cast<hipStream_t>(stream));
+  const qrs_status st = check_launch_bound();
+  if (st != QRS_OK) return st;
+  const hipError_t e = launch_in_parts(l, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -441,15 +562,23 @@ qrs_status qrs_quantize(int64_t tokens, int64_t h, qrs_x_dtype x_dtype, qrs_scal
   if (overlaps(x_bf16, 2 * n, x_codes, n) || overlaps(x_bf16, 2 * n, scales, scale_bytes) ||
       overlaps(x_codes, n, scales, scale_bytes))
     return fail(QRS_ERR_INVALID_ARG, "input, codes and scales must not overlap");
-  qrs::QuantizeLaunch l;
-  l.x_format = to_x_format(x_dtype);
-  l.scale_layout = f32_scales ? qrs::kScaleF32Group128 : qrs::kScaleE8M0Block32;
-  l.n_elems = n;
-  l.in = x_bf16;
-  l.codes = x_codes;
-  l.scales = scales;
-  const hipError_t e = qrs::launch_quantize(l, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  const qrs_status st = check_launch_bound();
+  if (st != QRS_OK) return st;
+  // Consecutive launches of at most max_launch_elems() elements, as for the
+  // reduce: groups never cross a launch's edge, whose scales start e0 / 32
+  // bytes on in both layouts.
+  const uint64_t m = max_launch_elems();
+  for (uint64_t e0 = 0; e0 < n; e0 += m) {
+    qrs::QuantizeLaunch l;
+    l.x_format = to_x_format(x_dtype);
+    l.scale_layout = f32_scales ? qrs::kScaleF32Group128 : qrs::kScaleE8M0Block32;
+    l.n_elems = n - e0 < m ? n - e0 : m;
+    l.in = static_cast<const char*>(x_bf16) + 2 * e0;
+    l.codes = static_cast<char*>(x_codes) + e0;
+    l.scales = static_cast<char*>(scales) + e0 / 32;
+    const hipError_t e = qrs::launch_quantize(l, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 
@@ -458,8 +587,12 @@ qrs_status qrs_stream_copy(const void* src, void* dst, size_t bytes, void* strea
   if (bytes == 0 || bytes % 16 != 0) return fail(QRS_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
   if (!aligned(src, 16) || !aligned(dst, 16)) return fail(QRS_ERR_INVALID_ARG, "pointers must be 16-byte aligned");
   if (overlaps(src, bytes, dst, bytes)) return fail(QRS_ERR_INVALID_ARG, "ranges overlap");
-  const hipError_t e = qrs::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  for (uint64_t b0 = 0; b0 < bytes; b0 += kMaxCopyBytes) {
+    const uint64_t nb = bytes - b0 < kMaxCopyBytes ? bytes - b0 : kMaxCopyBytes;
+    const hipError_t e = qrs::launch_stream_copy(static_cast<const char*>(src) + b0, static_cast<char*>(dst) + b0, nb,
+                                                 static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(QRS_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  }
   return ok();
 }
 
