@@ -137,6 +137,24 @@ def main():
     all_shares(4, 24, 2048, "e5m2", "e8m0_block32", "f16", 10)
     quantize(37, 1152, "e4m3fn", "e8m0_block32", 11)
     quantize(37, 1152, "int8", "f32_group128", 12)
+    # Seeded random shapes: every mode, W and output type, sizes from a few
+    # launches to a few dozen.
+    rng = np.random.default_rng(2024)
+    modes = [("int8", "f32_group128"), ("e4m3fn", "f32_group128"), ("e5m2", "f32_group128"),
+             ("e4m3fn", "e8m0_block32"), ("e5m2", "e8m0_block32")]
+    for i in range(12):
+        w = int(rng.choice([2, 4, 8]))
+        x_format, scale_layout = modes[int(rng.integers(len(modes)))]
+        out_dtype = str(rng.choice(["f32", "bf16", "f16"]))
+        h = 128 * int(rng.integers(8, 65))
+        rows = int(rng.integers(-(-2 * BOUND // h), 60))
+        kind = i % 3
+        if kind == 0:
+            contiguous(w, rows, h, x_format, scale_layout, out_dtype, 100 + i)
+        elif kind == 1:
+            strided(w, rows, h, x_format, scale_layout, out_dtype, 100 + i)
+        else:
+            all_shares(w, rows, h, x_format, scale_layout, out_dtype, 100 + i)
     print("[parts] all cases match the oracle", flush=True)
 
 

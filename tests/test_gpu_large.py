@@ -212,3 +212,20 @@ def test_quantize_in_two_launches(gpu, x_format, scale_layout):
         _equal_repeated(scales, torch.from_numpy(want_s).cuda(), "scales")
     del codes, scales
     torch.cuda.empty_cache()
+
+
+def test_stream_copy_past_2_35_bytes(gpu):
+    # The calibration copy runs as launches of 2^35 bytes (2^31 lanes of 16
+    # bytes): 2^35 + 2^20 bytes take two, the second starting 32 GiB in.
+    n = (1 << 35) + (1 << 20)
+    _free_or_skip(2 * n)
+    log(f"[large] stream copy of {n} bytes")
+    src = torch.arange(n // 8, dtype=torch.int64, device="cuda")
+    dst = torch.full_like(src, -1)
+    qrs.stream_copy(src, dst)
+    torch.cuda.synchronize()
+    step = 1 << 27
+    for i in range(0, n // 8, step):
+        assert torch.equal(dst[i:i + step], src[i:i + step]), f"words {i} to {i + step}"
+    del src, dst
+    torch.cuda.empty_cache()
