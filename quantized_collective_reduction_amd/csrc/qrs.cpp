@@ -209,7 +209,7 @@ qrs_status qrs_plan(int world_size, int64_t bs, int64_t h, qrs_x_dtype x_dtype, 
   if (!valid_h(h))
     return fail(QRS_ERR_INVALID_ARG, "h %lld: must be a multiple of 128 in [1024, 8192]", static_cast<long long>(h));
   const int64_t rows = bs / world_size;
-  // rows * h elements, each a 16-element chunk per lane; keep the launch in range.
+  // At most 2^40 elements per share (2^34 per launch: larger shares run as several launches).
   if (rows > (int64_t{1} << 40) / h) return fail(QRS_ERR_INVALID_ARG, "bs %lld too large", static_cast<long long>(bs));
 
   const qrs_status mode = check_mode(x_dtype, scale_layout);

@@ -69,7 +69,10 @@ struct ReduceLaunch {
 // kernels' index ranges: 2^39 or more chunks of 16 elements in a share;
 // for n_rows > 1 also rows or a row stride (in its units) of 2^32 or more,
 // a scale slice spanning 4 GiB or more, or a row of fewer than 64 or more
-// than 768 chunks.
+// than 768 chunks. The caller keeps one launch at or below 2^34 elements per
+// share (qrs.cpp splits larger shares into several launches): a HIP grid
+// holds fewer than 2^32 work-items along a dimension, and a lane takes 8 or
+// 16 elements.
 hipError_t launch_reduce(const ReduceLaunch& l, hipStream_t stream);
 
 // Whether an all-shares launch of this mode (n_shares = world_size) runs as
@@ -123,11 +126,12 @@ struct QuantizeLaunch {
   void* scales;    // 4-byte aligned for fp32
 };
 
+// At most 2^34 elements per launch, as for launch_reduce (qrs.cpp splits).
 hipError_t launch_quantize(const QuantizeLaunch& l, hipStream_t stream);
 
 // Plain 16-byte-per-lane device copy (bytes % 16 == 0, both pointers 16-byte
-// aligned): the reference stream for bandwidth and traffic-counter
-// calibration.
+// aligned, at most 2^35 bytes per launch): the reference stream for bandwidth
+// and traffic-counter calibration.
 hipError_t launch_stream_copy(const void* src, void* dst, uint64_t bytes, hipStream_t stream);
 
 }  // namespace qrs
