@@ -118,6 +118,75 @@ def quantize(tokens, h, x_format, scale_layout, seed):
         assert np.array_equal(got_s, want_s), what + ": scales"
 
 
+def _capture(fn):
+    """fn run once eagerly on a side stream, then captured in a graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def share_in_a_graph(w, rows, h, x_format, scale_layout, out_dtype, seed):
+    what = f"graph of a split share W={w} rows={rows} H={h} {x_format}/{scale_layout}->{out_dtype}"
+    log(f"[parts] {what}")
+    xs, ss = workloads.generate(_workload(w, rows, h, x_format, scale_layout, out_dtype, seed))
+    want = oracle_bits(oracle.reduce_scatter_share(xs, ss, x_format, scale_layout, out_dtype), out_dtype)
+    p = qrs.plan(w, rows * w, h, x_format, scale_layout, out_dtype)
+    assert qrs.run_launch_info(p)["launches"] > 1
+    dx, ds = to_device(xs, ss)
+    out = torch.empty((rows, h), dtype=OUT_TORCH[out_dtype], device="cuda")
+    g = _capture(lambda: qrs.run(p, dx, ds, out))
+    for rep in range(3):
+        out.fill_(float("nan"))  # eager work between replays: every element must be rewritten
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_parity(out_bits(out), want, out_dtype, f"{what}, replay {rep}")
+
+
+def pipeline_in_a_graph(w, rows, h, seed):
+    # Every rank's quantize, then the group's all shares, each split into
+    # several launches, in one graph.
+    what = f"graph of split quantizations and all shares W={w} rows={rows} H={h}"
+    log(f"[parts] {what}")
+    bs = w * rows
+    rng = np.random.default_rng(seed)
+    acts = []
+    for _ in range(w):
+        v = rng.standard_normal((bs, h)).astype(np.float32) * np.float32(4.0)
+        acts.append(torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    q = [oracle_quantize(a, "e4m3fn", "e8m0_block32") for a in acts]
+    want = oracle.all_shares([c for c, _ in q], [s for _, s in q], "e4m3fn", "e8m0_block32", "bf16")
+    xin = [torch.from_numpy(a.view(np.int16).copy()).view(torch.bfloat16).cuda() for a in acts]
+    p = qrs.plan(w, bs, h, "e4m3fn", "e8m0_block32", "bf16")
+    codes = [torch.empty((bs, h), dtype=torch.uint8, device="cuda") for _ in range(w)]
+    scales = [torch.empty((bs, h // 32), dtype=torch.uint8, device="cuda") for _ in range(w)]
+    outs = [torch.empty((rows, h), dtype=torch.bfloat16, device="cuda") for _ in range(w)]
+
+    def pipeline():
+        for r in range(w):
+            qrs.quantize(xin[r], codes[r], scales[r], "e4m3fn", "e8m0_block32")
+        qrs.run_all_shares(p, codes, scales, outs)
+
+    g = _capture(pipeline)
+    for rep in range(3):
+        for t in codes + scales:
+            t.fill_(0xAA)
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for j in range(w):
+            assert_parity(out_bits(outs[j]), oracle_bits(want[j], "bf16"), "bf16", f"{what}, replay {rep}, share {j}")
+
+
 def main():
     assert BOUND == 4096, "the cases below are sized for a bound of 4096 elements"
     # 42,624 elements: ten full launches and a ragged eleventh (1,664).
@@ -137,6 +206,9 @@ def main():
     all_shares(4, 24, 2048, "e5m2", "e8m0_block32", "f16", 10)
     quantize(37, 1152, "e4m3fn", "e8m0_block32", 11)
     quantize(37, 1152, "int8", "f32_group128", 12)
+    # Captured in HIP graphs: every launch of the split is a node.
+    share_in_a_graph(8, 37, 1152, "e4m3fn", "e8m0_block32", "bf16", 13)
+    pipeline_in_a_graph(4, 37, 1152, 14)
     # Seeded random shapes: every mode, W and output type, sizes from a few
     # launches to a few dozen.
     rng = np.random.default_rng(2024)
