@@ -58,7 +58,7 @@ typedef enum qrs_status {
   QRS_ERR_INVALID_ARG = 1, /* a parameter breaks a documented constraint   */
   QRS_ERR_UNSUPPORTED = 2, /* a format the library does not implement      */
   QRS_ERR_HIP = 3,         /* the HIP runtime reported an error at launch  */
-  QRS_ERR_OUT_OF_MEMORY = 4, /* a host allocation for a plan failed       */
+  QRS_ERR_OUT_OF_MEMORY = 4, /* a host allocation (plan, launch handle) failed */
   /* Range markers, not statuses: they make every int a value of the type,
    * so a caller may pass any int and the library rejects it as a value. */
   QRS_STATUS_RANGE_MIN_ = -2147483647 - 1,
